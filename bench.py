@@ -1,0 +1,234 @@
+"""Benchmark of the Qwen3-style decoder layer on one MI355X.
+
+A step is one full layer prefill (RMSNorm, QKV projection, QK-norm + RoPE + cache write,
+GQA causal attention, o_proj + residual, RMSNorm, gate/up + SwiGLU, down + residual) of the
+0.6B-shaped layer on one batch of B1 x T2048 synthetic tokens, inputs resident in HBM.
+Prints ONE JSON line: tokens/s of that step, the roofline fraction of its dominant kernel
+(per-kernel durations from HIP events recorded by the library around each launch, on the
+launch stream), the float64 CPU oracle timed on a bounded sample of the same workload, and,
+as extra context, the 8B-shaped layer prefill (B1 T8192) and the 8B-shaped decode step on a
+32768-key cache (decode attention achieved GB/s against HBM peak).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+METRIC = "Qwen3-layer prefill tokens/s & % MFMA peak; 32K decode attn % HBM BW"
+
+
+def layer_flops(cfg, b, t):
+    """Algorithmic FLOPs per launch of each prefill stage (2*M*N*K for projections; causal
+    attention counts 4*D*Hq*sum_t(t+1) over visible keys only)."""
+    m = b * t
+    h, d, hq, hkv, i = cfg.hidden_size, cfg.head_dim, cfg.num_attention_heads, cfg.num_key_value_heads, \
+        cfg.intermediate_size
+    return {
+        "gemm_qkv": 2.0 * m * (hq + 2 * hkv) * d * h,
+        "attention": 4.0 * d * hq * b * t * (t + 1) / 2,
+        "gemm_o_residual": 2.0 * m * h * hq * d,
+        "gemm_gate_up_swiglu": 2.0 * m * 2 * i * h,
+        "gemm_down_residual": 2.0 * m * h * i,
+    }
+
+
+def decode_attention_bytes(cfg, b, cached):
+    """Keys and values read once per decode step (each KV head read once for its g query
+    heads): 2 * B * Hkv * (cached + 1) * D * 2 bytes."""
+    return 2.0 * b * cfg.num_key_value_heads * (cached + 1) * cfg.head_dim * 2
+
+
+def setup_prefill(torch, si, nat, wl, device):
+    cfg = wl.cfg
+    g = torch.Generator(device=device).manual_seed(wl.seed)
+    dt = torch.bfloat16
+    w = {}
+    for name, shape in si.weight_shapes(cfg).items():
+        z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        w[name] = ((1 + 0.1 * z) if name in si.GAIN_NAMES else 0.02 * z).to(dt)
+    layer = nat.Layer(cfg, w)
+    x = torch.randn((wl.batch, wl.seq_len, cfg.hidden_size), generator=g, device=device).to(dt)
+    y = torch.empty_like(x)
+    cap = wl.seq_len + wl.cached
+    kc = torch.zeros((wl.batch, cfg.num_key_value_heads, cap, cfg.head_dim), dtype=dt, device=device)
+    vc = torch.zeros_like(kc)
+    ws = torch.empty(layer.workspace_size(wl.batch, wl.seq_len, cap), dtype=torch.uint8, device=device)
+    return layer, w, x, y, kc, vc, ws
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def profile_steps(torch, layer, fn, steps):
+    layer.set_profiling(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    prof = layer.read_profile()
+    layer.set_profiling(False)
+    return {k: v[1] / v[0] for k, v in prof.items()}     # average ms per launch
+
+
+def kernel_table(avg_ms, flops):
+    out = {}
+    for k, ms in avg_ms.items():
+        e = {"avg_ms": round(ms, 5)}
+        if k in flops:
+            tf = flops[k] / (ms * 1e-3) / 1e12
+            e.update(tflops=round(tf, 1), frac_of_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        out[k] = e
+    return out
+
+
+def bench_prefill(torch, si, nat, wl, steps, warmup, device):
+    layer, w, x, y, kc, vc, ws = setup_prefill(torch, si, nat, wl, device)
+    run = lambda: layer.prefill(x, y, kc, vc, ws)
+    ms = time_steps(torch, run, steps, warmup)
+    avg = profile_steps(torch, layer, run, steps)
+    flops = layer_flops(wl.cfg, wl.batch, wl.seq_len)
+    total = sum(flops.values())
+    res = dict(ms_per_step=ms, tokens_per_s=wl.batch * wl.seq_len / (ms * 1e-3),
+               layer_tflops=total / (ms * 1e-3) / 1e12, kernels=kernel_table(avg, flops))
+    dominant = max((k for k in avg if k in flops), key=lambda k: avg[k])
+    res["dominant"] = dominant
+    res["dominant_flops"] = flops[dominant]
+    res["dominant_ms"] = avg[dominant]
+    layer.close()
+    return res
+
+
+def bench_decode(torch, si, nat, wl, steps, warmup, device):
+    cfg = wl.cfg
+    layer, w, x, y, kc, vc, ws = setup_prefill(torch, si, nat, wl, device)
+    g = torch.Generator(device=device).manual_seed(wl.seed + 1)
+    n = wl.cached
+    kc[:, :, :n].copy_(torch.randn(kc[:, :, :n].shape, generator=g, device=device).to(kc.dtype))
+    vc[:, :, :n].copy_(torch.randn(vc[:, :, :n].shape, generator=g, device=device).to(vc.dtype))
+    lens = [n] * wl.batch
+    run = lambda: layer.decode(x, y, lens, kc, vc, ws)
+    ms = time_steps(torch, run, steps, warmup)
+    avg = profile_steps(torch, layer, run, steps)
+    attn_ms = avg["attention_decode_split"]
+    byts = decode_attention_bytes(cfg, wl.batch, n)
+    gbs = byts / (attn_ms * 1e-3) / 1e9
+    layer.close()
+    return dict(ms_per_step=ms, tokens_per_s=wl.batch / (ms * 1e-3), attention_ms=attn_ms,
+                attention_bytes=byts, attention_gbs=gbs, attention_frac_of_hbm_peak=gbs / PEAK_HBM_GBS,
+                kernels={k: {"avg_ms": round(v, 5)} for k, v in avg.items()})
+
+
+def cpu_baseline(si, wl, budget_s=30.0):
+    """The float64 oracle, untuned, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = wl.cfg
+    w = si.layer_weights(cfg, seed=wl.seed)
+    x = si.layer_input(cfg, wl.batch, wl.seq_len, seed=wl.seed)
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        oracle.layer_prefill(x, w, cfg)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el * (runs + 1) / runs > budget_s or runs >= 3:
+            break
+    tok_s = runs * wl.batch * wl.seq_len / el
+    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} full float64 oracle prefill(s) of the {wl.name} workload "
+                      f"(B{wl.batch} x T{wl.seq_len}), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 8B prefill and 32K decode measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import seeded_inputs as si
+    from transformer_decoder_layer_rmsnorm_amd import _native as nat
+    nat.lib()
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+
+    wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
+    print(f"[bench] {wl.name}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    res = bench_prefill(torch, si, nat, wl, args.steps, args.warmup, device)
+    dom_tf = res["dominant_flops"] / (res["dominant_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
+                   "hidden_size": wl.cfg.hidden_size, "heads": [wl.cfg.num_attention_heads,
+                                                                wl.cfg.num_key_value_heads],
+                   "head_dim": wl.cfg.head_dim, "intermediate_size": wl.cfg.intermediate_size},
+        "roofline": {"bound": "mfma", "kernel": res["dominant"], "achieved": round(dom_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "layer_tflops": round(res["layer_tflops"], 1),
+        "layer_frac_of_bf16_peak": round(res["layer_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "kernels": res["kernels"],
+    }
+    if not args.no_extra:
+        wl4 = si.WORKLOADS["qwen3-8b-layer-prefill"]
+        print(f"[bench] {wl4.name}", file=sys.stderr, flush=True)
+        r4 = bench_prefill(torch, si, nat, wl4, 10, 3, device)
+        line["qwen3_8b_layer_prefill"] = {
+            "tokens_per_s": round(r4["tokens_per_s"], 1), "ms_per_step": round(r4["ms_per_step"], 4),
+            "layer_tflops": round(r4["layer_tflops"], 1),
+            "layer_frac_of_bf16_peak": round(r4["layer_tflops"] / PEAK_BF16_TFLOPS, 4), "kernels": r4["kernels"]}
+        wl5 = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
+        print(f"[bench] {wl5.name}", file=sys.stderr, flush=True)
+        r5 = bench_decode(torch, si, nat, wl5, 20, 5, device)
+        line["decode_32k"] = {
+            "tokens_per_s": round(r5["tokens_per_s"], 1), "ms_per_step": round(r5["ms_per_step"], 4),
+            "roofline": {"bound": "hbm", "kernel": "attention_decode_split", "achieved": round(r5["attention_gbs"], 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r5["attention_frac_of_hbm_peak"], 4),
+                         "traffic": None},
+            "kernels": r5["kernels"]}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(si, wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

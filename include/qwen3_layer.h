@@ -1,0 +1,182 @@
+/*
+ * qwen3_layer.h - C ABI of a Qwen3-style pre-norm decoder layer on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer computes, for every token x of a sequence,
+ *   h    = RMSNorm_in(x)
+ *   q,k,v = h Wq^T, h Wk^T, h Wv^T                     (no biases)
+ *   qhat = RoPE_p(q_norm(q)), khat = RoPE_p(k_norm(k)) (per head, over head_dim)
+ *   o    = causal GQA attention(qhat, khat, v), scale head_dim^-1/2
+ *   x1   = x + o Wo^T
+ *   y    = x1 + down( silu(gate h2) * up h2 ),  h2 = RMSNorm_post(x1)
+ * as defined on "17. A modern architecture: Qwen3" (sections RMSNorm, Rotary
+ * position embeddings, Attention with grouped KV heads and Q/K normalization,
+ * SwiGLU, The whole model) and "Transformer architectures: from BERT to
+ * diffusion, lesson 6" (sections 3 and 5).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are caller-owned, contiguous, 16-byte aligned and hold the
+ *    configuration's dtype (bf16 or fp32) unless stated otherwise.  Weights use
+ *    the nn.Linear layout [out_features, in_features], row-major.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call is
+ *    asynchronous on it and never synchronises the host, except where noted.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    status other than QWEN3_OK nothing was launched (QWEN3_ERR_DEVICE excepted:
+ *    a launch failed after earlier kernels of the call were queued).
+ *    qwen3_last_error() describes the most recent failure of the calling thread.
+ *  - The library allocates no device memory after qwen3_layer_create: prefill
+ *    and decode use the caller's workspace.
+ */
+#ifndef QWEN3_LAYER_H
+#define QWEN3_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QWEN3_OK = 0,
+    QWEN3_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, odd head_dim, misalignment */
+    QWEN3_ERR_UNSUPPORTED = 2,        /* shape/dtype the kernels do not implement; Hq % Hkv != 0 */
+    QWEN3_ERR_OUT_OF_RANGE = 3,       /* tokens beyond the cache or max_position_embeddings */
+    QWEN3_ERR_WORKSPACE_TOO_SMALL = 4,
+    QWEN3_ERR_DEVICE = 5              /* a HIP call or kernel launch failed */
+} qwen3_status;
+
+typedef enum { QWEN3_F32 = 0, QWEN3_BF16 = 1 } qwen3_dtype;
+
+/* The per-layer fields of a Qwen3 config.json ("lesson 6", section 5, printed
+ * config; "17. A modern architecture: Qwen3", opening contract).  head_dim is
+ * its own field: Hq*head_dim need not equal hidden_size. */
+typedef struct {
+    int32_t hidden_size;
+    int32_t num_attention_heads;      /* Hq */
+    int32_t num_key_value_heads;      /* Hkv; Hq must be a multiple of it */
+    int32_t head_dim;                 /* D, even */
+    int32_t intermediate_size;        /* I */
+    int32_t max_position_embeddings;  /* positions must stay below this */
+    double  rope_theta;               /* RoPE base: omega_i = theta^(-2i/D) */
+    float   rms_norm_eps;             /* added to the mean square inside the root */
+    qwen3_dtype dtype;                /* storage type of weights, activations and cache */
+} qwen3_config;
+
+/* Device pointers to one layer's tensors (parameter names of the Qwen3
+ * checkpoint, "lesson 6" section 6).  Shapes: input_layernorm [H],
+ * q_proj [Hq*D, H], k_proj [Hkv*D, H], v_proj [Hkv*D, H], q_norm [D],
+ * k_norm [D], o_proj [H, Hq*D], post_attention_layernorm [H],
+ * gate_proj [I, H], up_proj [I, H], down_proj [H, I].
+ * The handle keeps these pointers (it does not copy or own the tensors): the
+ * caller keeps them alive and unchanged until qwen3_layer_destroy. */
+typedef struct {
+    const void *input_layernorm, *q_proj, *k_proj, *v_proj, *q_norm, *k_norm,
+               *o_proj, *post_attention_layernorm, *gate_proj, *up_proj, *down_proj;
+} qwen3_layer_weights;
+
+typedef struct qwen3_layer qwen3_layer;
+
+/* Byte offsets, inside the caller's workspace, of the intermediates a call
+ * leaves behind (M = batch * seq_len rows; es = 2 for bf16, 4 for fp32):
+ *   h     [M, H]            input RMSNorm output (dtype)
+ *   qkv   [M, (Hq+2Hkv)*D]  q | k | v projections, token-major (dtype)
+ *   qhat  [B, Hq, T, D]     normalised, rotated queries (dtype)
+ *   attn  [M, Hq*D]         attention output, token-major (dtype)
+ *   x1    [M, H]            residual after attention (always fp32)
+ *   h2    [M, H]            post-attention RMSNorm output (dtype)
+ *   act   [M, I]            silu(gate) * up (dtype)
+ *   lens  [B]               int32 copy of decode cache lengths
+ *   part_o  [B, Hq, S, D]   fp32 split-KV partial outputs (decode)
+ *   part_ml [B, Hq, S, 2]   fp32 split-KV running max (log2 units) and sum
+ * where S = number of key splits for cache_capacity keys. */
+typedef struct {
+    size_t h, qkv, qhat, attn, x1, h2, act, lens, part_o, part_ml;
+    size_t total;
+    int32_t decode_splits;   /* S */
+    int32_t split_keys;      /* keys per split */
+} qwen3_workspace_layout;
+
+/* Validates *config and *weights and returns a handle.  Host only: no HIP call
+ * is made, and the handle is not tied to a device - each call runs on the device
+ * that owns `stream` (the weights must live there).
+ * Errors: INVALID_ARGUMENT (null pointer, a size <= 0, odd head_dim, a weight
+ * pointer not 16-byte aligned), UNSUPPORTED (Hq % Hkv != 0 - the pages raise
+ * on it in Qwen3Attention; a dtype or head_dim the kernels lack: bf16 needs
+ * head_dim 128, fp32 head_dim <= 128; bf16 widths H, I, Hq*D, Hkv*D must be
+ * multiples of 128, 1/2/4/8 query heads per KV head). */
+qwen3_status qwen3_layer_create(const qwen3_config* config, const qwen3_layer_weights* weights,
+                                qwen3_layer** out_layer);
+
+/* Frees the handle (not the weights).  NULL is ignored. */
+void qwen3_layer_destroy(qwen3_layer* layer);
+
+/* Workspace bytes for a prefill of [batch, seq_len] tokens and for a decode
+ * of `batch` tokens over caches of `cache_capacity` slots (pass seq_len = 1
+ * for decode only).  Host only. */
+qwen3_status qwen3_layer_workspace_size(const qwen3_layer* layer, int32_t batch, int32_t seq_len,
+                                        int32_t cache_capacity, size_t* bytes);
+
+/* Offsets of the intermediates within that workspace (see the struct). */
+qwen3_status qwen3_layer_workspace_layout(const qwen3_layer* layer, int32_t batch, int32_t seq_len,
+                                          int32_t cache_capacity, qwen3_workspace_layout* layout);
+
+/* Prefill: x, y are [batch, seq_len, H]; token t of each sequence sits at
+ * position t (empty cache).  Writes khat and v of every token to slot t of
+ * k_cache / v_cache, laid out [batch, Hkv, cache_capacity, D] (keys are cached
+ * already rotated, "17. A modern architecture: Qwen3", end of Rotary position
+ * embeddings).  y may alias x.
+ * Errors: INVALID_ARGUMENT, OUT_OF_RANGE (seq_len > cache_capacity or
+ * seq_len > max_position_embeddings), WORKSPACE_TOO_SMALL, DEVICE. */
+qwen3_status qwen3_layer_prefill(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                 int32_t seq_len, void* k_cache, void* v_cache,
+                                 int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Decode: one new token per sequence; x, y are [batch, 1, H].  cache_lens is a
+ * HOST array [batch]: sequence b already holds cache_lens[b] rotated keys and
+ * values in slots 0..cache_lens[b]-1.  The new token is at position
+ * cache_lens[b], its khat / v are written to that slot and it attends keys
+ * 0..cache_lens[b] of its own sequence.  cache_lens is not modified (the caller
+ * advances it).  y may alias x.  Up to 64 sequences the lengths travel to the
+ * kernels as launch arguments; for more, they are copied into the workspace
+ * with hipMemcpyAsync.  Either way the host array may be reused once the call
+ * returns.
+ * Errors: INVALID_ARGUMENT, OUT_OF_RANGE (cache_lens[b] < 0,
+ * cache_lens[b] >= cache_capacity, cache_lens[b] >= max_position_embeddings),
+ * WORKSPACE_TOO_SMALL, DEVICE. */
+qwen3_status qwen3_layer_decode(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                const int32_t* cache_lens, void* k_cache, void* v_cache,
+                                int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* RMSNorm of `rows` rows of `width` elements ("17. A modern architecture:
+ * Qwen3", section RMSNorm): y = weight * x / sqrt(mean(x^2) + eps), reduced in
+ * fp32.  x, weight and y all hold `dtype`; used for the final norm after a
+ * stack of layers (section The whole model).  width must be a multiple of 8.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, DEVICE. */
+qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width,
+                           float eps, qwen3_dtype dtype, void* stream);
+
+/* Per-kernel timing of prefill / decode calls made while profiling is on:
+ * every launch is bracketed by two hipEvents on the call's stream. */
+typedef struct {
+    char name[48];
+    int32_t launches;
+    double total_ms;
+} qwen3_stage_time;
+
+qwen3_status qwen3_layer_set_profiling(qwen3_layer* layer, int32_t enabled);
+
+/* Waits for the recorded events (host synchronisation), returns the per-kernel
+ * totals accumulated since the last read, and clears them. */
+qwen3_status qwen3_layer_read_profile(qwen3_layer* layer, qwen3_stage_time* out,
+                                      int32_t max_entries, int32_t* n_entries);
+
+const char* qwen3_status_string(qwen3_status status);
+const char* qwen3_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QWEN3_LAYER_H */

@@ -79,11 +79,14 @@ WORKLOADS = {
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bf16 value (ties to even), returned as float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    """float32 -> nearest bf16 value (ties to even), returned as float32.  Finite inputs."""
+    u = np.array(a, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    u += lsb
+    u += 0x7FFF
+    u &= 0xFFFF0000
+    return u.view(np.float32)
 
 
 def _rng(seed: int, *keys: int) -> np.random.Generator:
@@ -140,3 +143,22 @@ def cache_block(cfg: LayerConfig, which: str, b: int, kv_head: int, n: int,
 
 def with_dtype(cfg: LayerConfig, dtype: str) -> LayerConfig:
     return replace(cfg, dtype=dtype)
+
+
+def fill_decode_cache(cfg: LayerConfig, batch: int, cached, sink, seed: int = 0, threads: int = 8) -> None:
+    """Draw the cached keys and values of every (sequence, KV head) in parallel and hand
+    each block to ``sink(b, kv_head, k_block, v_block)`` ([n, head_dim] arrays).
+    ``cached`` is one length for all sequences or a list of per-sequence lengths."""
+    import concurrent.futures
+
+    lens = [cached] * batch if np.isscalar(cached) else list(cached)
+
+    def one(item):
+        b, h = item
+        n = int(lens[b])
+        sink(b, h, cache_block(cfg, "k", b, h, n, seed), cache_block(cfg, "v", b, h, n, seed))
+
+    items = [(b, h) for b in range(batch) for h in range(cfg.num_key_value_heads)]
+    with concurrent.futures.ThreadPoolExecutor(max(1, threads)) as pool:
+        for _ in pool.map(one, items):
+            pass

@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: the library loads, exports every function include/*.h declares,
+and every validation error is returned on the host before anything is launched.
+Only host-side paths are exercised here (no kernel is ever launched)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import seeded_inputs as si
+from transformer_decoder_layer_rmsnorm_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000        # an aligned, never dereferenced stand-in for a device pointer
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(qwen3_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = nat.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", nat.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (qwen3_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    assert set(nat.EXPORTED) == set(names)
+
+
+def fake_weights():
+    return nat.Weights(*[FAKE] * len(nat.WEIGHT_NAMES))
+
+
+def create(cfg, weights=None):
+    c = nat.make_config(cfg)
+    h = ctypes.c_void_p()
+    st = nat.lib().qwen3_layer_create(ctypes.byref(c), ctypes.byref(weights or fake_weights()), ctypes.byref(h))
+    return st, h
+
+
+def err():
+    return nat.lib().qwen3_last_error().decode()
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=31), nat.QWEN3_ERR_INVALID_ARGUMENT),            # odd: no rotate-half pairing
+    (dict(hidden_size=0), nat.QWEN3_ERR_INVALID_ARGUMENT),
+    (dict(num_key_value_heads=-1), nat.QWEN3_ERR_INVALID_ARGUMENT),
+    (dict(rope_theta=0.0), nat.QWEN3_ERR_INVALID_ARGUMENT),
+    (dict(rms_norm_eps=-1e-6), nat.QWEN3_ERR_INVALID_ARGUMENT),
+    (dict(num_attention_heads=6, num_key_value_heads=4), nat.QWEN3_ERR_UNSUPPORTED),  # Hq % Hkv
+    (dict(hidden_size=60), nat.QWEN3_ERR_UNSUPPORTED),
+    (dict(head_dim=256), nat.QWEN3_ERR_UNSUPPORTED),
+])
+def test_create_rejects_bad_f32_configs(change, status):
+    cfg = si.LayerConfig(**{**si.TINY_F32.__dict__, **change})
+    st, h = create(cfg)
+    assert st == status, err()
+    assert not h.value
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(head_dim=64), nat.QWEN3_ERR_UNSUPPORTED),
+    (dict(intermediate_size=3000), nat.QWEN3_ERR_UNSUPPORTED),
+    (dict(num_attention_heads=48, num_key_value_heads=2), nat.QWEN3_ERR_UNSUPPORTED),  # g = 24
+])
+def test_create_rejects_unsupported_bf16_configs(change, status):
+    cfg = si.LayerConfig(**{**si.QWEN3_0P6B.__dict__, **change})
+    st, _ = create(cfg)
+    assert st == status, err()
+
+
+def test_create_rejects_null_and_misaligned_weights():
+    w = fake_weights()
+    w.q_norm = None
+    assert create(si.QWEN3_0P6B, w)[0] == nat.QWEN3_ERR_INVALID_ARGUMENT
+    w = fake_weights()
+    w.down_proj = FAKE + 2
+    assert create(si.QWEN3_0P6B, w)[0] == nat.QWEN3_ERR_INVALID_ARGUMENT
+    c = nat.make_config(si.QWEN3_0P6B)
+    assert nat.lib().qwen3_layer_create(ctypes.byref(c), None, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+
+
+@pytest.fixture
+def layer():
+    st, h = create(si.QWEN3_0P6B)
+    assert st == nat.QWEN3_OK, err()
+    yield h
+    nat.lib().qwen3_layer_destroy(h)
+
+
+def test_workspace_size_and_layout(layer):
+    L = nat.lib()
+    n = ctypes.c_size_t()
+    assert L.qwen3_layer_workspace_size(layer, 1, 2048, 2048, ctypes.byref(n)) == nat.QWEN3_OK
+    lay = nat.WorkspaceLayout()
+    assert L.qwen3_layer_workspace_layout(layer, 1, 2048, 2048, ctypes.byref(lay)) == nat.QWEN3_OK
+    m, h, i = 2048, 1024, 3072
+    # regions in order, 256-byte aligned, each large enough
+    offs = [lay.h, lay.qkv, lay.qhat, lay.attn, lay.x1, lay.h2, lay.act]
+    sizes = [m * h * 2, m * 4096 * 2, m * 2048 * 2, m * 2048 * 2, m * h * 4, m * h * 2, m * i * 2]
+    for k in range(len(offs)):
+        assert offs[k] % 256 == 0
+        if k + 1 < len(offs):
+            assert offs[k + 1] - offs[k] >= sizes[k]
+    assert n.value >= lay.act + sizes[-1]
+    assert lay.decode_splits == -(-2048 // lay.split_keys)
+    assert L.qwen3_layer_workspace_size(layer, 0, 5, 5, ctypes.byref(n)) == nat.QWEN3_ERR_INVALID_ARGUMENT
+
+
+def prefill(layer, b=1, t=16, cap=16, ws_bytes=1 << 30, x=FAKE, kc=FAKE):
+    return nat.lib().qwen3_layer_prefill(layer, x, FAKE, b, t, kc, FAKE, cap, FAKE, ws_bytes, None)
+
+
+def test_prefill_validation_before_launch(layer):
+    assert prefill(layer, t=17, cap=16) == nat.QWEN3_ERR_OUT_OF_RANGE           # T > capacity
+    assert prefill(layer, t=40961, cap=50000) == nat.QWEN3_ERR_OUT_OF_RANGE     # T > max positions
+    assert prefill(layer, ws_bytes=1000) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+    assert prefill(layer, x=None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert prefill(layer, kc=FAKE + 8) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert prefill(layer, b=0) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert prefill(layer, t=-3) == nat.QWEN3_ERR_INVALID_ARGUMENT
+
+
+def decode(layer, lens, cap=64, ws_bytes=1 << 30):
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    return nat.lib().qwen3_layer_decode(layer, FAKE, FAKE, len(lens), arr, FAKE, FAKE, cap, FAKE, ws_bytes, None)
+
+
+def test_decode_validation_before_launch(layer):
+    assert decode(layer, [10, 64]) == nat.QWEN3_ERR_OUT_OF_RANGE       # no free slot
+    assert decode(layer, [10, -1]) == nat.QWEN3_ERR_OUT_OF_RANGE
+    assert decode(layer, [40960], cap=50000) == nat.QWEN3_ERR_OUT_OF_RANGE   # position limit
+    assert decode(layer, [3, 4], ws_bytes=100) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+    assert nat.lib().qwen3_layer_decode(layer, FAKE, FAKE, 1, None, FAKE, FAKE, 8, FAKE, 1 << 30, None) \
+        == nat.QWEN3_ERR_INVALID_ARGUMENT
+
+
+def test_rmsnorm_validation_and_status_strings():
+    L = nat.lib()
+    assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 4, 12, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_UNSUPPORTED
+    assert L.qwen3_rmsnorm(None, FAKE, FAKE, 4, 16, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 0, 16, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    for s in range(6):
+        assert L.qwen3_status_string(s)
+    assert "unknown" in L.qwen3_status_string(99).decode()
+
+
+def test_python_binding_raises_with_message():
+    with pytest.raises(nat.Qwen3Error) as e:
+        nat.check(nat.QWEN3_ERR_OUT_OF_RANGE, "probe")
+    assert e.value.status == nat.QWEN3_ERR_OUT_OF_RANGE

@@ -1,0 +1,214 @@
+"""GPU parity of the HIP path against the float64 oracle on small and ragged shapes.
+
+Every call goes through the C ABI (Python binding).  Kernel-level tests feed the oracle
+step the GPU's own input ("teacher forcing"), so each kernel is judged alone; layer tests
+compare the whole layer with the oracle on the same seeded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_support import (GpuLayer, assert_bf16_parity, assert_f32_parity, assert_rounded, check_decode_steps, log,
+                         oracle_qk_from_proj, small_bf16_cfg, to_dev, to_np)
+from transformer_decoder_layer_rmsnorm_amd import _native as nat
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- RMSNorm entry point
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,width", [(1, 64), (7, 1024), (1000, 4096), (33, 5120), (5, 8)])
+def test_rmsnorm_kernel(dtype, rows, width):
+    log(f"rmsnorm {dtype} rows={rows} width={width}")
+    cfg = si.LayerConfig(hidden_size=width, num_attention_heads=1, num_key_value_heads=1, head_dim=2,
+                         intermediate_size=8, dtype=dtype)
+    rng = np.random.default_rng(rows * 7 + width)
+    x = si.round_to_bf16(rng.standard_normal((rows, width)).astype(np.float32) * 3) if dtype == "bf16" else \
+        rng.standard_normal((rows, width)).astype(np.float32) * 3
+    g = si.round_to_bf16((1 + 0.1 * rng.standard_normal(width)).astype(np.float32))
+    xd, gd = to_dev(x, cfg), to_dev(g, cfg)
+    y = torch.empty_like(xd)
+    nat.rmsnorm(xd, gd, y, 1e-6)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x, g, 1e-6)
+    if dtype == "bf16":
+        assert_rounded(to_np(y), ref, "rmsnorm bf16", abs_frac=1e-6)
+    else:
+        np.testing.assert_allclose(to_np(y), ref, rtol=2e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- fp32 layer (tiny config)
+
+def test_tiny_f32_layer_matches_oracle():
+    wl = si.WORKLOADS["tiny-f32-layer"]
+    cfg = wl.cfg
+    log(f"tiny fp32 layer B{wl.batch} T{wl.seq_len}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed)
+    x = si.layer_input(cfg, wl.batch, wl.seq_len, seed=wl.seed)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    ref = oracle.layer_prefill(x, gl.w_np, cfg)
+    assert_f32_parity(to_np(y), ref["y"], "y")
+    inter = gl.intermediates(ws, wl.batch, wl.seq_len)
+    for name in ["h", "qhat", "attn", "x1", "h2", "act"]:
+        assert_f32_parity(inter[name], ref[name], name)
+    assert_f32_parity(to_np(kc)[:, :, : wl.seq_len], ref["khat"], "k cache")
+    assert_f32_parity(to_np(vc)[:, :, : wl.seq_len], ref["v"], "v cache")
+
+
+@pytest.mark.parametrize("b,t,hq,hkv,d", [(2, 37, 4, 4, 64), (3, 5, 8, 2, 16), (1, 130, 6, 3, 128)])
+def test_f32_layer_shapes(b, t, hq, hkv, d):
+    cfg = si.LayerConfig(hidden_size=96, num_attention_heads=hq, num_key_value_heads=hkv, head_dim=d,
+                         intermediate_size=136, dtype="f32")
+    log(f"fp32 layer B{b} T{t} Hq{hq} Hkv{hkv} D{d}")
+    gl = GpuLayer.seeded(cfg, seed=3)
+    x = si.layer_input(cfg, b, t, seed=3)
+    y, *_ = gl.prefill(to_dev(x, cfg), cap=t + 3)
+    assert_f32_parity(to_np(y), oracle.layer_prefill(x, gl.w_np, cfg)["y"], "y")
+
+
+def test_f32_decode_continues_prefill():
+    cfg = si.TINY_F32
+    gl = GpuLayer.seeded(cfg, seed=5)
+    b, t = 3, 12
+    x = si.layer_input(cfg, b, t, seed=5)
+    full = oracle.layer_prefill(x, gl.w_np, cfg)
+    lens = [11, 4, 0]
+    cap = 16
+    kc, vc = gl.alloc_cache(b, cap)
+    for i, n in enumerate(lens):
+        if n:
+            gl.prefill(to_dev(x[i:i + 1, :n], cfg), caches=(kc[i:i + 1], vc[i:i + 1]), cap=cap)
+    xin = np.stack([x[i, n] for i, n in enumerate(lens)])[:, None]
+    y, _ = gl.decode(to_dev(xin, cfg), lens, kc, vc)
+    for i, n in enumerate(lens):
+        assert_f32_parity(to_np(y)[i, 0], full["y"][i, n], f"decode row {i} at position {n}")
+
+
+# ---------------------------------------------------------------- bf16 kernels, teacher-forced
+
+@pytest.mark.parametrize("hq,hkv,b,t", [(4, 2, 2, 77), (4, 4, 1, 130), (8, 2, 1, 200), (16, 2, 1, 64), (4, 1, 2, 33)])
+def test_bf16_kernels_teacher_forced(hq, hkv, b, t):
+    cfg = small_bf16_cfg(hq=hq, hkv=hkv)
+    log(f"bf16 kernels Hq{hq} Hkv{hkv} B{b} T{t}")
+    gl = GpuLayer.seeded(cfg, seed=hq * 10 + hkv)
+    w = gl.w_np
+    x = si.layer_input(cfg, b, t, seed=hq + t)
+    cap = t + 5
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg), cap=cap)
+    it = gl.intermediates(ws, b, t)
+    eps = cfg.rms_norm_eps
+    kcn, vcn = to_np(kc), to_np(vc)
+    for s in range(b):
+        assert_rounded(it["h"][s], oracle.rmsnorm(x[s], w["input_layernorm"], eps), "rmsnorm_input")
+        wqkv = np.concatenate([w["q_proj"], w["k_proj"], w["v_proj"]]).astype(np.float64)
+        assert_rounded(it["qkv"][s], it["h"][s] @ wqkv.T, "gemm_qkv")
+        qhat, khat, v = oracle_qk_from_proj(it["qkv"][s], w, cfg, np.arange(t))
+        assert_rounded(it["qhat"][s], qhat, "qknorm_rope q")
+        assert_rounded(kcn[s, :, :t], khat, "qknorm_rope k -> cache")
+        assert np.array_equal(vcn[s, :, :t], v), "v copied to the cache unchanged"
+        attn = oracle.gqa_causal_attention(it["qhat"][s], kcn[s, :, :t], vcn[s, :, :t], np.arange(t), np.arange(t))
+        attn = attn.transpose(1, 0, 2).reshape(t, hq * 128)
+        assert_bf16_parity(it["attn"][s], attn, "attention (bf16 probabilities)")
+        x1 = x[s] + it["attn"][s] @ w["o_proj"].T.astype(np.float64)
+        np.testing.assert_allclose(it["x1"][s], x1, rtol=1e-5, atol=2e-5)
+        assert_rounded(it["h2"][s], oracle.rmsnorm(it["x1"][s], w["post_attention_layernorm"], eps), "rmsnorm_post")
+        act = oracle.silu(it["h2"][s] @ w["gate_proj"].T.astype(np.float64)) * \
+            (it["h2"][s] @ w["up_proj"].T.astype(np.float64))
+        assert_rounded(it["act"][s], act, "gemm_gate_up_swiglu")
+        yref = it["x1"][s] + it["act"][s] @ w["down_proj"].T.astype(np.float64)
+        assert_rounded(to_np(y)[s], yref, "gemm_down_residual")
+
+
+@pytest.mark.parametrize("hq,hkv,b,t", [(4, 2, 2, 77), (8, 8, 1, 96), (8, 1, 1, 150)])
+def test_bf16_layer_matches_oracle(hq, hkv, b, t):
+    cfg = small_bf16_cfg(hq=hq, hkv=hkv)
+    log(f"bf16 layer Hq{hq} Hkv{hkv} B{b} T{t}")
+    gl = GpuLayer.seeded(cfg, seed=7)
+    x = si.layer_input(cfg, b, t, seed=7)
+    y, *_ = gl.prefill(to_dev(x, cfg))
+    assert_bf16_parity(to_np(y), oracle.layer_prefill(x, gl.w_np, cfg)["y"], "y")
+
+
+def test_bf16_causality_bit_exact():
+    cfg = small_bf16_cfg()
+    gl = GpuLayer.seeded(cfg, seed=9)
+    t = 150
+    x = si.layer_input(cfg, 1, t, seed=9)
+    y0, *_ = gl.prefill(to_dev(x, cfg))
+    y0 = y0.clone()
+    for i in [0, 63, 64, 100, 148]:
+        x2 = x.copy()
+        x2[0, i + 1:] = si.round_to_bf16(np.random.default_rng(i).standard_normal(x2[0, i + 1:].shape)
+                                         .astype(np.float32))
+        y2, *_ = gl.prefill(to_dev(x2, cfg))
+        assert torch.equal(y0[0, : i + 1], y2[0, : i + 1]), f"rows <= {i} changed"
+        assert not torch.equal(y0[0, i + 1:], y2[0, i + 1:])
+    log("  causality: rows up to i are bit-identical under changes after i")
+
+
+def test_bf16_output_may_alias_input():
+    cfg = small_bf16_cfg()
+    gl = GpuLayer.seeded(cfg, seed=11)
+    x = si.layer_input(cfg, 2, 40, seed=11)
+    y, *_ = gl.prefill(to_dev(x, cfg))
+    xd = to_dev(x, cfg)
+    gl.prefill(xd, y_dev=xd)
+    assert torch.equal(xd, y)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (8, 8)])
+def test_bf16_decode_matches_oracle_ragged(hq, hkv):
+    cfg = small_bf16_cfg(hq=hq, hkv=hkv)
+    gl = GpuLayer.seeded(cfg, seed=13)
+    lens = [0, 1, 511, 512, 513, 1500, 37]
+    b = len(lens)
+    cap = 1600
+    log(f"bf16 decode Hq{hq} Hkv{hkv} lens {lens}")
+    kc = np.zeros((b, hkv, cap, 128), np.float32)
+    vc = np.zeros((b, hkv, cap, 128), np.float32)
+    for i, n in enumerate(lens):
+        for h in range(hkv):
+            kc[i, h, :n] = si.cache_block(cfg, "k", i, h, n, seed=13)
+            vc[i, h, :n] = si.cache_block(cfg, "v", i, h, n, seed=13)
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    x = si.layer_input(cfg, b, 1, seed=13)
+    y, ws = gl.decode(to_dev(x, cfg), lens, kd, vd)
+    ref, _, _ = oracle.layer_decode(x, gl.w_np, cfg, kc, vc, lens)
+    assert_bf16_parity(to_np(y), ref, "decode y")
+    check_decode_steps(gl, ws, lens, kd, vd)
+
+
+def test_bf16_decode_continues_prefill():
+    cfg = small_bf16_cfg()
+    gl = GpuLayer.seeded(cfg, seed=17)
+    t = 300
+    x = si.layer_input(cfg, 1, t, seed=17)
+    yfull, *_ = gl.prefill(to_dev(x, cfg))
+    cap = t + 8
+    kc, vc = gl.alloc_cache(1, cap)
+    gl.prefill(to_dev(x[:, : t - 1], cfg), caches=(kc, vc), cap=cap)
+    y, _ = gl.decode(to_dev(x[:, t - 1: t], cfg), [t - 1], kc, vc)
+    ref = oracle.layer_prefill_rows(x, gl.w_np, cfg, [(0, t - 1)])
+    assert_bf16_parity(to_np(y)[0, 0], ref[0], "decode row vs oracle")
+    assert_bf16_parity(to_np(y)[0, 0], to_np(yfull)[0, t - 1], "decode row vs prefill row")
+
+
+def test_profiling_reports_every_stage():
+    cfg = small_bf16_cfg()
+    gl = GpuLayer.seeded(cfg, seed=19)
+    x = to_dev(si.layer_input(cfg, 1, 128, seed=19), cfg)
+    gl.layer.set_profiling(True)
+    for _ in range(3):
+        gl.prefill(x)
+    prof = gl.layer.read_profile()
+    gl.layer.set_profiling(False)
+    names = {"rmsnorm_input", "gemm_qkv", "qknorm_rope", "attention", "gemm_o_residual", "rmsnorm_post",
+             "gemm_gate_up_swiglu", "gemm_down_residual"}
+    assert names <= set(prof), prof
+    for n in names:
+        launches, ms = prof[n]
+        assert launches == 3 and ms > 0
+    assert gl.layer.read_profile() == {}

@@ -1,0 +1,154 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+  * 0.6B-shaped layer, B1 T2048: every output element against the oracle.
+  * 8B-shaped layer, B1 T8192: sampled rows (the oracle computes keys/values for all
+    tokens and the rest only for the sampled rows).
+  * 8B-shaped decode, 16 sequences on 32768 cached keys: every output row.
+  * 0.6B-shaped 28-layer stack, B4 T4096: each layer teacher-forced (the oracle layer fed
+    the GPU's bf16 input of that layer) on sampled rows, plus the final norm; the same
+    stack in fp32 end to end at a small length; the bf16 end-to-end drift is reported.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_support import (GpuLayer, assert_bf16_parity, assert_f32_parity, assert_rounded, bf16_metrics,
+                         check_decode_steps, log, to_dev, to_np)
+from transformer_decoder_layer_rmsnorm_amd import _native as nat
+
+pytestmark = pytest.mark.gpu
+
+
+def test_qwen3_0p6b_layer_prefill_every_row():
+    wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
+    cfg = wl.cfg
+    log(f"{wl.name}: B{wl.batch} T{wl.seq_len}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed)
+    x = si.layer_input(cfg, wl.batch, wl.seq_len, seed=wl.seed)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    ref = oracle.layer_prefill(x, gl.w_np, cfg)
+    assert_bf16_parity(to_np(y), ref["y"], "y")
+    it = gl.intermediates(ws, wl.batch, wl.seq_len)
+    assert_bf16_parity(it["x1"], ref["x1"], "x1 (fp32 residual)")
+    assert_bf16_parity(to_np(kc), ref["khat"], "k cache")
+
+
+def test_qwen3_8b_layer_prefill_sampled_rows():
+    wl = si.WORKLOADS["qwen3-8b-layer-prefill"]
+    cfg = wl.cfg
+    log(f"{wl.name}: B{wl.batch} T{wl.seq_len}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed)
+    x = si.layer_input(cfg, wl.batch, wl.seq_len, seed=wl.seed)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    rng = np.random.default_rng(1)
+    ts = sorted(set([0, 1, 31, 32, 63, 64, 127, 128, 1000, 2047, 4095, 4096, 6000, 8190, 8191] +
+                    list(rng.integers(0, wl.seq_len, 9))))
+    rows = [(0, t) for t in ts]
+    ref = oracle.layer_prefill_rows(x, gl.w_np, cfg, rows)
+    got = to_np(y)[0, ts]
+    assert_bf16_parity(got, ref, f"y at {len(ts)} sampled rows")
+
+
+def test_qwen3_8b_decode_32k_every_row():
+    wl = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
+    cfg = wl.cfg
+    b, n = wl.batch, wl.cached
+    cap = n + 1
+    log(f"{wl.name}: B{b}, {n} cached keys, capacity {cap}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed)
+    shape = (b, cfg.num_key_value_heads, cap, cfg.head_dim)
+    kc = np.zeros(shape, np.float32)
+    vc = np.zeros(shape, np.float32)
+
+    def sink(i, h, kb, vb):
+        kc[i, h, :n] = kb
+        vc[i, h, :n] = vb
+
+    si.fill_decode_cache(cfg, b, n, sink, seed=wl.seed)
+    log("  cache generated")
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    x = si.layer_input(cfg, b, 1, seed=wl.seed)
+    y, ws = gl.decode(to_dev(x, cfg), [n] * b, kd, vd)
+    ref, _, _ = oracle.layer_decode(x, gl.w_np, cfg, kc, vc, [n] * b)
+    assert_bf16_parity(to_np(y), ref, "decode y (16 rows)")
+    del kc, vc
+    check_decode_steps(gl, ws, [n] * b, kd, vd)
+
+
+def test_qwen3_0p6b_stack28_teacher_forced():
+    wl = si.WORKLOADS["qwen3-0.6b-stack28-prefill"]
+    cfg = wl.cfg
+    b, t = wl.batch, wl.seq_len
+    log(f"{wl.name}: B{b} T{t}, {wl.layers} layers + final norm")
+    x = si.layer_input(cfg, b, t, seed=wl.seed)
+    cur = to_dev(x, cfg)
+    kc = vc = ws = None
+    rng = np.random.default_rng(2)
+    worst = None
+    for layer in range(wl.layers):
+        gl = GpuLayer.seeded(cfg, layer=layer, seed=wl.seed)
+        if kc is None:
+            kc, vc = gl.alloc_cache(b, t)
+            ws = gl.workspace(b, t, t)
+        y, *_ = gl.prefill(cur, caches=(kc, vc), ws=ws)
+        seqs = [layer % b, (layer + 2) % b]
+        rows = [(s, int(r)) for s in seqs for r in [0, t - 1, rng.integers(1, t - 1)]]
+        xin = to_np(cur)
+        ref = oracle.layer_prefill_rows(xin, gl.w_np, cfg, rows)
+        got = np.stack([to_np(y[s, r]) for s, r in rows])
+        m = assert_bf16_parity(got, ref, f"layer {layer} (teacher-forced, rows {rows})")
+        worst = m if worst is None or m["mean_rel"] > worst["mean_rel"] else worst
+        cur = y
+        del gl
+    gain = si.final_norm_gain(cfg, seed=wl.seed)
+    gd = to_dev(gain, cfg)
+    out = torch.empty_like(cur)
+    nat.rmsnorm(cur, gd, out, cfg.rms_norm_eps)
+    torch.cuda.synchronize()
+    assert_rounded(to_np(out), oracle.rmsnorm(to_np(cur), gain, cfg.rms_norm_eps), "final norm (teacher-forced)")
+    log(f"  worst layer mean_rel {worst['mean_rel']:.3g}, max_abs {worst['max_abs']:.3g}")
+
+
+def run_stack(cfg, x, layers, seed, gain):
+    cur = to_dev(x, cfg)
+    b, t, _ = x.shape
+    kc = vc = ws = None
+    for layer in range(layers):
+        gl = GpuLayer.seeded(cfg, layer=layer, seed=seed)
+        if kc is None:
+            kc, vc = gl.alloc_cache(b, t)
+            ws = gl.workspace(b, t, t)
+        cur, *_ = gl.prefill(cur, caches=(kc, vc), ws=ws)
+    out = torch.empty_like(cur)
+    nat.rmsnorm(cur, to_dev(gain, cfg), out, cfg.rms_norm_eps)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+def test_stack28_fp32_end_to_end():
+    cfg = si.with_dtype(si.QWEN3_0P6B, "f32")
+    b, t, layers = 2, 48, 28
+    log(f"fp32 stack of {layers} 0.6B-shaped layers, B{b} T{t}")
+    x = si.layer_input(cfg, b, t, seed=4)
+    gain = si.final_norm_gain(cfg, seed=4)
+    got = run_stack(cfg, x, layers, 4, gain)
+    ws = [si.layer_weights(cfg, layer=l, seed=4) for l in range(layers)]
+    ref = oracle.stack_prefill(x, ws, gain, cfg)
+    assert_f32_parity(got, ref, "final-normed output")
+
+
+def test_stack28_bf16_end_to_end_drift_reported():
+    cfg = si.QWEN3_0P6B
+    b, t, layers = 1, 256, 28
+    x = si.layer_input(cfg, b, t, seed=6)
+    gain = si.final_norm_gain(cfg, seed=6)
+    got = run_stack(cfg, x, layers, 6, gain)
+    ws = [si.layer_weights(cfg, layer=l, seed=6) for l in range(layers)]
+    ref = oracle.stack_prefill(x, ws, gain, cfg, round_between=si.round_to_bf16)
+    m = bf16_metrics(got, ref)
+    log(f"  bf16 28-layer end-to-end drift (reported, not gated): max_abs {m['max_abs']:.3g}, "
+        f"mean_rel {m['mean_rel']:.3g}")
+    assert np.all(np.isfinite(got))
+    assert m["mean_rel"] < 0.05   # gross-error guard only

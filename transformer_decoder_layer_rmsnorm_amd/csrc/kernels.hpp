@@ -1,0 +1,97 @@
+// Host-side launch interface of the gfx950 kernels (one .hip file per kernel family).
+// Every launcher only enqueues work on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q3 {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// Position of token 0 of each sequence (== the cache slot it is written to).  Prefill on an
+// empty cache uses all zeros; decode passes the cache lengths, by value for up to
+// kInlinePositions sequences (no host-to-device copy), else through a device array.
+constexpr int kInlinePositions = 64;
+struct SeqPositions {
+    const int32_t* dev;                 // device array [B], or nullptr
+    int32_t n_inline;                   // when dev == nullptr: inl[b] for b < n_inline, else 0
+    int32_t inl[kInlinePositions];
+};
+__device__ __forceinline__ int seq_pos(const SeqPositions& p, int b) {
+    return p.dev ? p.dev[b] : (b < p.n_inline ? p.inl[b] : 0);
+}
+
+inline int dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- RMSNorm
+// y[r, :] = g * x[r, :] / sqrt(mean(x[r, :]^2) + eps), fp32 reduction, one rounding.
+hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt,
+                          int64_t rows, int width, float eps, hipStream_t stream);
+
+// ---------------------------------------------------------------- projections (C = A * B^T)
+enum class Epilogue : int {
+    Store = 0,         // out(dtype)  = C
+    ResidToF32 = 1,    // out(fp32)   = resid(dtype) + C        (o_proj: x1 = x + attn Wo^T)
+    SwiGLU = 2,        // out(dtype)  = silu(C_gate) * C_up     (B0 = gate, B1 = up)
+    ResidF32In = 3,    // out(dtype)  = resid(fp32) + C         (down: y = x1 + act Wd^T)
+};
+
+struct GemmArgs {
+    const void* a;          // [M, K] row-major, dtype
+    const void* b[3];       // weight segments, each [rows, K] row-major (nn.Linear layout)
+    int b_rows[3];          // rows of each segment; segments are stacked along N
+    int nseg;
+    void* out;              // [M, N] row-major (N = sum of segment rows, or I for SwiGLU)
+    const void* resid;      // [M, N] residual for the two residual epilogues
+    int M, N, K;
+    Epilogue epi;
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& args, hipStream_t stream);   // MFMA, large M
+hipError_t launch_gemv_bf16(const GemmArgs& args, hipStream_t stream);   // MFMA, M <= 64
+hipError_t launch_gemm_f32(const GemmArgs& args, hipStream_t stream);    // fp32 FMA, any shape
+bool gemm_bf16_supported(int N_segment_rows, int K);
+
+// ---------------------------------------------------------------- QK-norm + RoPE + cache write
+struct QkRopeArgs {
+    const void* qkv;        // [M, (Hq + 2 Hkv) D] token-major projections
+    const void* q_norm;     // [D]
+    const void* k_norm;     // [D]
+    void* qhat;             // [B, Hq, T, D]
+    void* k_cache;          // [B, Hkv, cap, D]
+    void* v_cache;          // [B, Hkv, cap, D]
+    SeqPositions pos;       // position (and cache slot) of token 0 of each sequence
+    int B, T, Hq, Hkv, D, cap;
+    double theta;
+    float eps;
+};
+hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+    const void* qhat;       // [B, Hq, T, D]
+    const void* k_cache;    // [B, Hkv, cap, D]
+    const void* v_cache;    // [B, Hkv, cap, D]
+    void* out;              // [B, T, Hq, D] (token-major rows of width Hq * D)
+    SeqPositions pos;       // position of query 0 of each sequence
+    int B, T, Hq, Hkv, D, cap;
+    float scale;            // D^-1/2
+};
+// Causal prefill: query t of sequence b sits at position pos0(b) + t and sees keys 0 .. pos.
+hipError_t launch_attention_prefill_bf16(const AttnArgs& args, hipStream_t stream);
+// Generic fp32 attention (any D <= 128), prefill or decode (T = 1).
+hipError_t launch_attention_f32(const AttnArgs& args, hipStream_t stream);
+
+// Split-KV decode (T = 1): partials then combine.
+struct DecodeAttnArgs {
+    AttnArgs a;
+    float* part_o;          // [B, Hq, S, D]
+    float* part_ml;         // [B, Hq, S, 2]
+    int splits;             // S
+    int split_keys;
+};
+hipError_t launch_attention_decode_split_bf16(const DecodeAttnArgs& args, hipStream_t stream);
+hipError_t launch_attention_decode_combine_bf16(const DecodeAttnArgs& args, hipStream_t stream);
+constexpr int kDecodeSplitKeys = 512;
+
+}  // namespace q3

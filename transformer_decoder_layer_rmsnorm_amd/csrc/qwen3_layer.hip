@@ -1,0 +1,479 @@
+// C ABI of the Qwen3-style decoder layer: argument validation, workspace layout and the
+// kernel sequence of prefill and decode.  Declarations and contracts: include/qwen3_layer.h.
+//
+// Kernel sequence of one layer ("17. A modern architecture: Qwen3", section The whole model:
+// x = x + attn(input_layernorm(x)); x = x + mlp(post_attention_layernorm(x))):
+//   1 rmsnorm        x  -> h
+//   2 gemm (store)   h  -> qkv          q | k | v projections in one pass over the three weights
+//   3 qknorm_rope    qkv -> qhat, k/v cache slots
+//   4 attention      qhat, cache -> attn
+//   5 gemm (+resid)  attn, x -> x1 (fp32 residual stream)
+//   6 rmsnorm        x1 -> h2
+//   7 gemm (swiglu)  h2 -> act = silu(h2 Wg^T) * (h2 Wu^T)
+//   8 gemm (+resid)  act, x1 -> y
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/qwen3_layer.h"
+#include "kernels.hpp"
+
+using namespace q3;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qwen3_status fail(qwen3_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+qwen3_status fail(qwen3_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct StageRec {
+    int stage;
+    hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct qwen3_layer {
+    qwen3_config cfg;
+    qwen3_layer_weights w;
+    bool profiling = false;
+    std::mutex prof_mu;
+    std::vector<std::string> stage_names;
+    std::vector<StageRec> pending;
+    std::vector<hipEvent_t> free_events;
+};
+
+namespace {
+
+DType dt(const qwen3_config& c) { return c.dtype == QWEN3_BF16 ? DType::BF16 : DType::F32; }
+
+qwen3_status validate_config(const qwen3_config* c) {
+    if (!c) return fail(QWEN3_ERR_INVALID_ARGUMENT, "config is NULL");
+    if (c->hidden_size <= 0 || c->num_attention_heads <= 0 || c->num_key_value_heads <= 0 ||
+        c->head_dim <= 0 || c->intermediate_size <= 0 || c->max_position_embeddings <= 0)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "config sizes must be positive");
+    if (c->head_dim % 2)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "head_dim %d is odd: RoPE pairs feature i with i + head_dim/2",
+                    c->head_dim);
+    if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "rope_theta must be positive and finite");
+    if (!(c->rms_norm_eps >= 0.f) || !std::isfinite(c->rms_norm_eps))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "rms_norm_eps must be non-negative and finite");
+    if (c->dtype != QWEN3_F32 && c->dtype != QWEN3_BF16)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)c->dtype);
+    if (c->num_attention_heads % c->num_key_value_heads)
+        return fail(QWEN3_ERR_UNSUPPORTED, "num_attention_heads %d is not a multiple of num_key_value_heads %d",
+                    c->num_attention_heads, c->num_key_value_heads);
+    const int64_t H = c->hidden_size, D = c->head_dim, I = c->intermediate_size;
+    const int64_t Hq = c->num_attention_heads, Hkv = c->num_key_value_heads;
+    if (H % 8) return fail(QWEN3_ERR_UNSUPPORTED, "hidden_size must be a multiple of 8");
+    if ((Hq + 2 * Hkv) * D >= (int64_t)1 << 30 || H * I >= (int64_t)1 << 31 || H * Hq * D >= (int64_t)1 << 31)
+        return fail(QWEN3_ERR_UNSUPPORTED, "layer too large for 32-bit weight indexing");
+    if (c->dtype == QWEN3_BF16) {
+        if (D != 128) return fail(QWEN3_ERR_UNSUPPORTED, "bf16 kernels need head_dim 128 (got %d)", (int)D);
+        const int g = (int)(Hq / Hkv);
+        if (g != 1 && g != 2 && g != 4 && g != 8)
+            return fail(QWEN3_ERR_UNSUPPORTED, "bf16 decode supports 1, 2, 4 or 8 query heads per KV head (got %d)", g);
+        if (H % 128 || I % 128)
+            return fail(QWEN3_ERR_UNSUPPORTED, "bf16 kernels need hidden_size and intermediate_size multiples of 128");
+    } else {
+        if (D > 128) return fail(QWEN3_ERR_UNSUPPORTED, "fp32 kernels need head_dim <= 128 (got %d)", (int)D);
+    }
+    return QWEN3_OK;
+}
+
+struct Layout {
+    size_t h, qkv, qhat, attn, x1, h2, act, prefill_end;
+    size_t lens, part_o, part_ml, total;
+    int splits;
+};
+
+Layout make_layout(const qwen3_config& c, int64_t B, int64_t T, int64_t cap) {
+    const int64_t M = B * T;
+    const int64_t es = c.dtype == QWEN3_BF16 ? 2 : 4;
+    const int64_t H = c.hidden_size, D = c.head_dim, I = c.intermediate_size;
+    const int64_t Hq = c.num_attention_heads, Hkv = c.num_key_value_heads;
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    L.h = take(M * H * es);
+    L.qkv = take(M * (Hq + 2 * Hkv) * D * es);
+    L.qhat = take(M * Hq * D * es);
+    L.attn = take(M * Hq * D * es);
+    L.x1 = take(M * H * 4);
+    L.h2 = take(M * H * es);
+    L.act = take(M * I * es);
+    L.prefill_end = off;
+    L.splits = cap > 0 ? (int)((cap + kDecodeSplitKeys - 1) / kDecodeSplitKeys) : 0;
+    L.lens = take(B * 4);
+    L.part_o = take(c.dtype == QWEN3_BF16 ? B * Hq * L.splits * D * 4 : 0);
+    L.part_ml = take(c.dtype == QWEN3_BF16 ? B * Hq * L.splits * 2 * 4 : 0);
+    L.total = off;
+    return L;
+}
+
+qwen3_status check_sizes(const qwen3_layer* L, int32_t batch, int32_t seq_len, int32_t cap) {
+    if (!L) return fail(QWEN3_ERR_INVALID_ARGUMENT, "layer is NULL");
+    if (batch <= 0 || seq_len <= 0) return fail(QWEN3_ERR_INVALID_ARGUMENT, "batch and seq_len must be positive");
+    if (cap < 0) return fail(QWEN3_ERR_INVALID_ARGUMENT, "cache_capacity must be non-negative");
+    const qwen3_config& c = L->cfg;
+    const int64_t M = (int64_t)batch * seq_len;
+    const int64_t widest = std::max<int64_t>({(int64_t)c.intermediate_size,
+                                              (int64_t)(c.num_attention_heads + 2 * c.num_key_value_heads) * c.head_dim,
+                                              (int64_t)c.hidden_size});
+    if (M * widest >= (int64_t)1 << 31)
+        return fail(QWEN3_ERR_UNSUPPORTED, "batch*seq_len too large for 32-bit activation indexing");
+    if ((int64_t)batch * c.num_key_value_heads * std::max(cap, seq_len) * c.head_dim >= (int64_t)1 << 40)
+        return fail(QWEN3_ERR_UNSUPPORTED, "cache too large");
+    return QWEN3_OK;
+}
+
+// ------------------------------------------------------------------ profiling helpers
+hipEvent_t take_event(qwen3_layer* L) {
+    if (!L->free_events.empty()) {
+        hipEvent_t e = L->free_events.back();
+        L->free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+int stage_id(qwen3_layer* L, const char* name) {
+    for (size_t i = 0; i < L->stage_names.size(); ++i)
+        if (L->stage_names[i] == name) return (int)i;
+    L->stage_names.emplace_back(name);
+    return (int)L->stage_names.size() - 1;
+}
+
+template <typename F>
+qwen3_status run_stage(qwen3_layer* L, const char* name, hipStream_t s, F&& launch) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (L->profiling) {
+        std::lock_guard<std::mutex> g(L->prof_mu);
+        e0 = take_event(L);
+        e1 = take_event(L);
+        if (e0) hipEventRecord(e0, s);
+    }
+    const hipError_t err = launch();
+    if (err != hipSuccess) return fail(QWEN3_ERR_DEVICE, "%s: %s", name, hipGetErrorString(err));
+    if (L->profiling && e0 && e1) {
+        std::lock_guard<std::mutex> g(L->prof_mu);
+        hipEventRecord(e1, s);
+        L->pending.push_back({stage_id(L, name), e0, e1});
+    }
+    return QWEN3_OK;
+}
+
+GemmArgs gemm(const void* a, std::initializer_list<const void*> b, std::initializer_list<int> rows, void* out,
+              const void* resid, int M, int N, int K, Epilogue epi) {
+    GemmArgs g{};
+    g.a = a;
+    int i = 0;
+    for (const void* p : b) g.b[i++] = p;
+    g.nseg = i;
+    i = 0;
+    for (int r : rows) g.b_rows[i++] = r;
+    g.out = out;
+    g.resid = resid;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.epi = epi;
+    return g;
+}
+
+// The whole layer on M = B*T tokens.  `pos` gives the position of token 0 of each sequence.
+qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, void* kc, void* vc, int cap,
+                       char* ws, const Layout& lay, const SeqPositions& pos, bool decode, hipStream_t s) {
+    const qwen3_config& c = L->cfg;
+    const DType t = dt(c);
+    const int M = B * T, H = c.hidden_size, D = c.head_dim, I = c.intermediate_size;
+    const int Hq = c.num_attention_heads, Hkv = c.num_key_value_heads;
+    const bool bf = t == DType::BF16;
+    void* h = ws + lay.h;
+    void* qkv = ws + lay.qkv;
+    void* qhat = ws + lay.qhat;
+    void* attn = ws + lay.attn;
+    void* x1 = ws + lay.x1;
+    void* h2 = ws + lay.h2;
+    void* act = ws + lay.act;
+    const float eps = c.rms_norm_eps;
+    auto proj = [&](const GemmArgs& g) {
+        if (!bf) return launch_gemm_f32(g, s);
+        return g.M <= 64 ? launch_gemv_bf16(g, s) : launch_gemm_bf16(g, s);
+    };
+    qwen3_status st;
+#define STAGE(name, expr)                                    \
+    if ((st = run_stage(L, name, s, [&]() { return (expr); })) != QWEN3_OK) return st;
+
+    STAGE("rmsnorm_input", launch_rmsnorm(x, t, L->w.input_layernorm, h, t, M, H, eps, s));
+    STAGE("gemm_qkv", proj(gemm(h, {L->w.q_proj, L->w.k_proj, L->w.v_proj}, {Hq * D, Hkv * D, Hkv * D}, qkv, nullptr,
+                                M, (Hq + 2 * Hkv) * D, H, Epilogue::Store)));
+    QkRopeArgs qa{};
+    qa.qkv = qkv;
+    qa.q_norm = L->w.q_norm;
+    qa.k_norm = L->w.k_norm;
+    qa.qhat = qhat;
+    qa.k_cache = kc;
+    qa.v_cache = vc;
+    qa.pos = pos;
+    qa.B = B;
+    qa.T = T;
+    qa.Hq = Hq;
+    qa.Hkv = Hkv;
+    qa.D = D;
+    qa.cap = cap;
+    qa.theta = c.rope_theta;
+    qa.eps = eps;
+    STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
+    AttnArgs aa{};
+    aa.qhat = qhat;
+    aa.k_cache = kc;
+    aa.v_cache = vc;
+    aa.out = attn;
+    aa.pos = pos;
+    aa.B = B;
+    aa.T = T;
+    aa.Hq = Hq;
+    aa.Hkv = Hkv;
+    aa.D = D;
+    aa.cap = cap;
+    aa.scale = (float)(1.0 / std::sqrt((double)D));
+    if (!bf) {
+        STAGE("attention", launch_attention_f32(aa, s));
+    } else if (decode) {
+        DecodeAttnArgs da{};
+        da.a = aa;
+        da.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+        da.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
+        da.splits = lay.splits;
+        da.split_keys = kDecodeSplitKeys;
+        STAGE("attention_decode_split", launch_attention_decode_split_bf16(da, s));
+        STAGE("attention_decode_combine", launch_attention_decode_combine_bf16(da, s));
+    } else {
+        STAGE("attention", launch_attention_prefill_bf16(aa, s));
+    }
+    STAGE("gemm_o_residual", proj(gemm(attn, {L->w.o_proj}, {H}, x1, x, M, H, Hq * D, Epilogue::ResidToF32)));
+    STAGE("rmsnorm_post", launch_rmsnorm(x1, DType::F32, L->w.post_attention_layernorm, h2, t, M, H, eps, s));
+    STAGE("gemm_gate_up_swiglu", proj(gemm(h2, {L->w.gate_proj, L->w.up_proj}, {I, I}, act, nullptr, M, I, H,
+                                           Epilogue::SwiGLU)));
+    STAGE("gemm_down_residual", proj(gemm(act, {L->w.down_proj}, {H}, y, x1, M, H, I, Epilogue::ResidF32In)));
+#undef STAGE
+    return QWEN3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qwen3_status_string(qwen3_status s) {
+    switch (s) {
+        case QWEN3_OK: return "ok";
+        case QWEN3_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case QWEN3_ERR_UNSUPPORTED: return "unsupported";
+        case QWEN3_ERR_OUT_OF_RANGE: return "out of range";
+        case QWEN3_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case QWEN3_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char* qwen3_last_error(void) { return g_last_error.c_str(); }
+
+qwen3_status qwen3_layer_create(const qwen3_config* config, const qwen3_layer_weights* weights,
+                                qwen3_layer** out_layer) {
+    if (!out_layer) return fail(QWEN3_ERR_INVALID_ARGUMENT, "out_layer is NULL");
+    *out_layer = nullptr;
+    qwen3_status st = validate_config(config);
+    if (st != QWEN3_OK) return st;
+    if (!weights) return fail(QWEN3_ERR_INVALID_ARGUMENT, "weights is NULL");
+    const void* ptrs[] = {weights->input_layernorm, weights->q_proj, weights->k_proj, weights->v_proj,
+                          weights->q_norm, weights->k_norm, weights->o_proj, weights->post_attention_layernorm,
+                          weights->gate_proj, weights->up_proj, weights->down_proj};
+    for (const void* p : ptrs) {
+        if (!p) return fail(QWEN3_ERR_INVALID_ARGUMENT, "a weight pointer is NULL");
+        if (!aligned16(p)) return fail(QWEN3_ERR_INVALID_ARGUMENT, "weight pointers must be 16-byte aligned");
+    }
+    qwen3_layer* L = new qwen3_layer();
+    L->cfg = *config;
+    L->w = *weights;
+    *out_layer = L;
+    return QWEN3_OK;
+}
+
+void qwen3_layer_destroy(qwen3_layer* L) {
+    if (!L) return;
+    for (auto& r : L->pending) {
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    for (hipEvent_t e : L->free_events) hipEventDestroy(e);
+    delete L;
+}
+
+qwen3_status qwen3_layer_workspace_size(const qwen3_layer* L, int32_t batch, int32_t seq_len, int32_t cap,
+                                        size_t* bytes) {
+    if (!bytes) return fail(QWEN3_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    qwen3_status st = check_sizes(L, batch, seq_len, cap);
+    if (st != QWEN3_OK) return st;
+    *bytes = std::max(make_layout(L->cfg, batch, seq_len, 0).prefill_end, make_layout(L->cfg, batch, 1, cap).total);
+    return QWEN3_OK;
+}
+
+qwen3_status qwen3_layer_workspace_layout(const qwen3_layer* L, int32_t batch, int32_t seq_len, int32_t cap,
+                                          qwen3_workspace_layout* out) {
+    if (!out) return fail(QWEN3_ERR_INVALID_ARGUMENT, "layout is NULL");
+    qwen3_status st = check_sizes(L, batch, seq_len, cap);
+    if (st != QWEN3_OK) return st;
+    const Layout lay = make_layout(L->cfg, batch, seq_len, cap);
+    out->h = lay.h;
+    out->qkv = lay.qkv;
+    out->qhat = lay.qhat;
+    out->attn = lay.attn;
+    out->x1 = lay.x1;
+    out->h2 = lay.h2;
+    out->act = lay.act;
+    out->lens = lay.lens;
+    out->part_o = lay.part_o;
+    out->part_ml = lay.part_ml;
+    out->total = lay.total;
+    out->decode_splits = lay.splits;
+    out->split_keys = kDecodeSplitKeys;
+    return QWEN3_OK;
+}
+
+qwen3_status qwen3_layer_prefill(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                 void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    qwen3_status st = check_sizes(L, batch, seq_len, cache_capacity);
+    if (st != QWEN3_OK) return st;
+    if (!x || !y || !k_cache || !v_cache || !workspace)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, y, k_cache, v_cache and workspace must be non-NULL");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    if (seq_len > cache_capacity)
+        return fail(QWEN3_ERR_OUT_OF_RANGE, "seq_len %d exceeds cache_capacity %d", seq_len, cache_capacity);
+    if (seq_len > L->cfg.max_position_embeddings)
+        return fail(QWEN3_ERR_OUT_OF_RANGE, "seq_len %d exceeds max_position_embeddings %d", seq_len,
+                    L->cfg.max_position_embeddings);
+    const Layout lay = make_layout(L->cfg, batch, seq_len, 0);
+    if (workspace_bytes < lay.prefill_end)
+        return fail(QWEN3_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, prefill needs %zu", workspace_bytes,
+                    lay.prefill_end);
+    SeqPositions pos{};
+    return run_layer(L, x, y, batch, seq_len, k_cache, v_cache, cache_capacity, static_cast<char*>(workspace), lay,
+                     pos, false, static_cast<hipStream_t>(stream));
+}
+
+qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
+                                void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    qwen3_status st = check_sizes(L, batch, 1, cache_capacity);
+    if (st != QWEN3_OK) return st;
+    if (!x || !y || !k_cache || !v_cache || !workspace || !cache_lens)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, y, cache_lens, k_cache, v_cache and workspace must be non-NULL");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    for (int b = 0; b < batch; ++b) {
+        const int n = cache_lens[b];
+        if (n < 0 || n >= cache_capacity)
+            return fail(QWEN3_ERR_OUT_OF_RANGE, "cache_lens[%d] = %d leaves no free slot in a cache of %d", b, n,
+                        cache_capacity);
+        if (n >= L->cfg.max_position_embeddings)
+            return fail(QWEN3_ERR_OUT_OF_RANGE, "position %d of sequence %d reaches max_position_embeddings %d", n, b,
+                        L->cfg.max_position_embeddings);
+    }
+    const Layout lay = make_layout(L->cfg, batch, 1, cache_capacity);
+    if (workspace_bytes < lay.total)
+        return fail(QWEN3_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, decode needs %zu", workspace_bytes,
+                    lay.total);
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SeqPositions pos{};
+    if (batch <= kInlinePositions) {
+        pos.n_inline = batch;
+        for (int b = 0; b < batch; ++b) pos.inl[b] = cache_lens[b];
+    } else {
+        const hipError_t e = hipMemcpyAsync(ws + lay.lens, cache_lens, sizeof(int32_t) * batch, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying cache_lens: %s", hipGetErrorString(e));
+        pos.dev = reinterpret_cast<const int32_t*>(ws + lay.lens);
+    }
+    return run_layer(L, x, y, batch, 1, k_cache, v_cache, cache_capacity, ws, lay, pos, true, s);
+}
+
+qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width, float eps,
+                           qwen3_dtype dtype, void* stream) {
+    if (!x || !weight || !y) return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, weight and y must be non-NULL");
+    if (rows <= 0 || width <= 0) return fail(QWEN3_ERR_INVALID_ARGUMENT, "rows and width must be positive");
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(y))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+    if (dtype != QWEN3_F32 && dtype != QWEN3_BF16) return fail(QWEN3_ERR_INVALID_ARGUMENT, "unknown dtype");
+    if (width % 8) return fail(QWEN3_ERR_UNSUPPORTED, "width must be a multiple of 8");
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(QWEN3_ERR_INVALID_ARGUMENT, "eps must be non-negative");
+    const DType t = dtype == QWEN3_BF16 ? DType::BF16 : DType::F32;
+    const hipError_t e = launch_rmsnorm(x, t, weight, y, t, rows, width, eps, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "rmsnorm: %s", hipGetErrorString(e));
+    return QWEN3_OK;
+}
+
+qwen3_status qwen3_layer_set_profiling(qwen3_layer* L, int32_t enabled) {
+    if (!L) return fail(QWEN3_ERR_INVALID_ARGUMENT, "layer is NULL");
+    L->profiling = enabled != 0;
+    return QWEN3_OK;
+}
+
+qwen3_status qwen3_layer_read_profile(qwen3_layer* L, qwen3_stage_time* out, int32_t max_entries, int32_t* n) {
+    if (!L || !n || (max_entries > 0 && !out)) return fail(QWEN3_ERR_INVALID_ARGUMENT, "NULL argument");
+    std::lock_guard<std::mutex> g(L->prof_mu);
+    std::vector<double> total(L->stage_names.size(), 0.0);
+    std::vector<int> count(L->stage_names.size(), 0);
+    qwen3_status st = QWEN3_OK;
+    for (auto& r : L->pending) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) st = fail(QWEN3_ERR_DEVICE, "profile events: %s", hipGetErrorString(e));
+        total[r.stage] += ms;
+        count[r.stage] += 1;
+        L->free_events.push_back(r.start);
+        L->free_events.push_back(r.stop);
+    }
+    L->pending.clear();
+    int k = 0;
+    for (size_t i = 0; i < L->stage_names.size(); ++i) {
+        if (!count[i]) continue;
+        if (k < max_entries) {
+            std::memset(out[k].name, 0, sizeof(out[k].name));
+            std::strncpy(out[k].name, L->stage_names[i].c_str(), sizeof(out[k].name) - 1);
+            out[k].launches = count[i];
+            out[k].total_ms = total[i];
+        }
+        ++k;
+    }
+    *n = std::min(k, max_entries);
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// RMSNorm, one 64-lane wavefront per row.
+//
+// "17. A modern architecture: Qwen3", section RMSNorm: y_i = g_i x_i / sqrt(mean_j x_j^2 + eps),
+// mean of squares in fp32 whatever the storage type.  Here the normalised value is multiplied
+// by the gain in fp32 and rounded once to the output type (the page rounds to the input type
+// before the gain; the difference is below one output ulp).
+//
+// Memory-bound: each row is read once (16-byte loads, kept in registers up to 4096 wide) and
+// written once.  Four rows per 256-thread workgroup.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace q3 {
+
+template <typename TX, typename TY, int MAXC>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, const TY* __restrict__ g,
+                                                      TY* __restrict__ y, int64_t rows, int width, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const TX* xr = x + row * width;
+    TY* yr = y + row * width;
+    const int nchunk = width >> 3;   // chunks of 8 elements
+
+    if (MAXC > 0 && nchunk <= MAXC * kWave) {
+        float v[MAXC][8];
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = lane + j * kWave;
+            if (c < nchunk) {
+                load8(xr + c * 8, v[j]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+            }
+        }
+        const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = lane + j * kWave;
+            if (c < nchunk) {
+                float gv[8], o[8];
+                load8(g + c * 8, gv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = gv[i] * (v[j][i] * rstd);
+                store8(yr + c * 8, o);
+            }
+        }
+    } else {
+        float ss = 0.f;
+        for (int c = lane; c < nchunk; c += kWave) {
+            float v[8];
+            load8(xr + c * 8, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+        }
+        const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
+        for (int c = lane; c < nchunk; c += kWave) {
+            float v[8], gv[8], o[8];
+            load8(xr + c * 8, v);
+            load8(g + c * 8, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = gv[i] * (v[i] * rstd);
+            store8(yr + c * 8, o);
+        }
+    }
+}
+
+template <typename TX, typename TY>
+static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
+                               hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    rmsnorm_kernel<TX, TY, 8><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
+                                                   static_cast<TY*>(y), rows, width, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt, int64_t rows, int width,
+                          float eps, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (xt == DType::BF16 && yt == DType::BF16) return launch_typed<bf16, bf16>(x, g, y, rows, width, eps, stream);
+    if (xt == DType::F32 && yt == DType::BF16) return launch_typed<float, bf16>(x, g, y, rows, width, eps, stream);
+    if (xt == DType::F32 && yt == DType::F32) return launch_typed<float, float>(x, g, y, rows, width, eps, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace q3
