@@ -134,7 +134,7 @@ def bench_decode(torch, si, nat, wl, steps, warmup, device):
                 kernels={k: {"avg_ms": round(v, 5)} for k, v in avg.items()})
 
 
-def cpu_baseline(si, wl, budget_s=30.0):
+def cpu_baseline(si, wl, min_s=10.0, budget_s=30.0):
     """The float64 oracle, untuned, on a bounded sample of the same workload."""
     import oracle
     try:
@@ -151,7 +151,7 @@ def cpu_baseline(si, wl, budget_s=30.0):
         oracle.layer_prefill(x, w, cfg)
         runs += 1
         el = time.perf_counter() - t0
-        if el * (runs + 1) / runs > budget_s or runs >= 3:
+        if el >= min_s or el * (runs + 1) / runs > budget_s:
             break
     tok_s = runs * wl.batch * wl.seq_len / el
     return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 8B prefill and 32K decode measurements")
+    ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of the 8B prefill / decode runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -178,6 +181,16 @@ def main():
     nat.lib()
     device = "cuda:0"
     torch.cuda.set_device(0)
+
+    calib = None
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        ms = time_steps(torch, lambda: dst.copy_(src), 5, 1)
+        calib = {"bytes_read": n, "bytes_written": n, "avg_ms": round(ms, 4),
+                 "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+        del src, dst
 
     wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
     print(f"[bench] {wl.name}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
@@ -210,20 +223,22 @@ def main():
     if not args.no_extra:
         wl4 = si.WORKLOADS["qwen3-8b-layer-prefill"]
         print(f"[bench] {wl4.name}", file=sys.stderr, flush=True)
-        r4 = bench_prefill(torch, si, nat, wl4, 10, 3, device)
+        r4 = bench_prefill(torch, si, nat, wl4, args.extra_steps, 3, device)
         line["qwen3_8b_layer_prefill"] = {
             "tokens_per_s": round(r4["tokens_per_s"], 1), "ms_per_step": round(r4["ms_per_step"], 4),
             "layer_tflops": round(r4["layer_tflops"], 1),
             "layer_frac_of_bf16_peak": round(r4["layer_tflops"] / PEAK_BF16_TFLOPS, 4), "kernels": r4["kernels"]}
         wl5 = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
         print(f"[bench] {wl5.name}", file=sys.stderr, flush=True)
-        r5 = bench_decode(torch, si, nat, wl5, 20, 5, device)
+        r5 = bench_decode(torch, si, nat, wl5, 2 * args.extra_steps, 5, device)
         line["decode_32k"] = {
             "tokens_per_s": round(r5["tokens_per_s"], 1), "ms_per_step": round(r5["ms_per_step"], 4),
             "roofline": {"bound": "hbm", "kernel": "attention_decode_split", "achieved": round(r5["attention_gbs"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r5["attention_frac_of_hbm_peak"], 4),
                          "traffic": None},
             "kernels": r5["kernels"]}
+    if calib:
+        line["copy_calibration"] = calib
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(si, wl)
