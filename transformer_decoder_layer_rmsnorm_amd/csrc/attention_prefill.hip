@@ -9,18 +9,25 @@
 // the softmax is accumulated online (running max and sum per query, rescaling the output).
 //
 // Layout choices for CDNA4:
-//  * A workgroup (4 waves) serves several query heads of ONE KV head (up to 4), so each K/V
-//    tile staged in LDS is read by every head of its group (the fused-kernel point of the GQA
-//    section: one read of a shared KV head serves g query heads).  Each wave owns 32 queries of
-//    one head.
+//  * A workgroup (4 waves) serves up to 4 query heads of ONE KV head, so each K/V tile staged in
+//    LDS is read by every head of its group (one read of a shared KV head serves g query heads).
+//    Each wave owns 32 queries of one head.  Two workgroups share a CU (<= 256 registers per
+//    lane, 80 KB of LDS each), so one workgroup's softmax overlaps the other's matrix work.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: in the 32x32
-//    accumulator a lane holds 16 keys of ONE query (column = lane % 32), so the row max and
-//    sum of the softmax are per-lane reductions plus one exchange with lane ^ 32.
-//  * The probabilities stay in registers and feed O^T += V^T P^T directly as the B operand.
-//    V^T is produced while staging V into LDS (4 keys x 8 dims per thread, packed into 8-byte
-//    cells), with a cell swizzle that keeps both the transposed stores and the fragment reads
-//    free of bank conflicts.
-//  * K rows in LDS are 256 bytes with the 16-byte chunk index XOR-swizzled by the key.
+//    accumulator a lane holds 16 keys of ONE query (column = lane % 32), so the row max is a
+//    per-lane reduction plus one exchange with lane ^ 32.
+//  * The probabilities stay in registers and feed O^T += V^T P^T directly as the B operand.  V
+//    stays row-major in LDS; its A-operand fragments come from ds_read_b64_tr_b16 transpose reads
+//    whose per-lane row choice reproduces the accumulator's key order (4 consecutive keys from
+//    each lane half, see v_frag below), so no register transpose is needed.
+//  * LDS rows are padded (K 272 B, V 320 B) so fragment reads hit all 64 banks once and every
+//    fragment address is a per-lane base plus an immediate.
+//  * K and V tiles are fetched with buffer loads whose descriptor covers exactly the visible
+//    keys: the hardware returns zeros past the end, so the last tile needs no clamping.
+//  * The output is rescaled only when some lane's running max grows by more than 8 (log2
+//    units): the reference max may lag the true max, which only bounds the probabilities by
+//    2^8 and cancels in the final normalisation.  The row sum accumulates the bf16-rounded
+//    probabilities the PV product actually uses (v_dot2), so the weights sum exactly to one.
 //  * Tiles above the diagonal are never visited; per wave, 32-key blocks that lie entirely
 //    above its queries skip their MFMAs.  The heaviest query tiles are dispatched first.
 #include "common.hpp"
@@ -30,20 +37,31 @@ namespace q3 {
 
 namespace {
 
-constexpr int HD = 128;  // head_dim
-constexpr int KT = 64;   // keys per tile
+constexpr int HD = 128;               // head_dim
+constexpr int KT = 64;                // keys per tile
+constexpr int KP = HD + 8;            // K row pitch in elements (272 B)
+constexpr int VP = HD + 32;           // V row pitch in elements (320 B)
+constexpr int K_ELEMS = KT * KP;
+constexpr int V_ELEMS = KT * VP;
+constexpr int NT = 256;               // threads per workgroup (4 waves)
+constexpr int CH = (KT * HD / 8) / NT;  // 16-byte chunks of K (and of V) staged per thread
 
-__device__ __forceinline__ int k_off(int key, int chunk) { return key * HD + ((chunk ^ (key & 7)) << 3); }
-__device__ __forceinline__ int vt_off(int d, int cell) {
-    return d * KT + ((cell ^ ((d & 15) ^ ((d >> 3) & 15))) << 2);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
 template <int HPW>
-__global__ __launch_bounds__(256) void flash_prefill_kernel(AttnArgs a, float scale_log2) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a,
+                                                                                                   float scale_log2) {
     constexpr int WPH = 4 / HPW;       // waves per head
     constexpr int QB = 32 * WPH;       // queries per workgroup
-    __shared__ __attribute__((aligned(16))) bf16 sK[2][KT * HD];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][HD * KT];
+    __shared__ __attribute__((aligned(16))) bf16 sK[2 * K_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2 * V_ELEMS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = a.Hq / a.Hkv;
@@ -53,9 +71,9 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(AttnArgs a, float sc
     const int b = blockIdx.z;
     const int nqt = (a.T + QB - 1) / QB;
     const int q0 = (nqt - 1 - (int)blockIdx.x) * QB;
-    const int qw = q0 + (wave % WPH) * 32;          // first query index of this wave
-    const int pos0 = seq_pos(a.pos, b);
-    const int kv_len = pos0 + min(q0 + QB, a.T);    // keys 0 .. last query position of the group
+    const int qw = q0 + (wave % WPH) * 32;                        // first query index of this wave
+    const int pos0 = __builtin_amdgcn_readfirstlane(seq_pos(a.pos, b));
+    const int kv_len = pos0 + min(q0 + QB, a.T);                  // keys 0 .. last query position
     const int ntiles = (kv_len + KT - 1) / KT;
     const int my_pos = pos0 + qw + (lane & 31);
     const int wave_first = pos0 + qw;
@@ -70,38 +88,41 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(AttnArgs a, float sc
         for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + (2 * s + (lane >> 5)) * 8);
     }
 
+    // Buffer descriptors over keys 0 .. kv_len-1 of this (sequence, KV head).
     const int64_t kv_base = ((int64_t)b * a.Hkv + kvh) * a.cap * HD;
-    const bf16* kg = static_cast<const bf16*>(a.k_cache) + kv_base;
-    const bf16* vg = static_cast<const bf16*>(a.v_cache) + kv_base;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.k_cache) + kv_base), (short)0, kv_len * HD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.v_cache) + kv_base), (short)0, kv_len * HD * 2, 0x00020000);
 
-    bf16x8 rk[4], rv[4];
-    auto gload = [&](int kt) {
-        const int k0 = kt * KT;
+    // Staging: thread moves 16-byte chunk st_ch of keys st_row + 16 j, j < CH.
+    const int st_row = tid >> 4, st_ch = tid & 15;
+    int4v rk[CH], rv[CH];
+    auto gload = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tid + 256 * j;
-            const int key = min(k0 + (c >> 4), kv_len - 1);
-            rk[j] = *reinterpret_cast<const bf16x8*>(kg + (int64_t)key * HD + (c & 15) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = min(k0 + (tid >> 4) * 4 + i, kv_len - 1);
-            rv[i] = *reinterpret_cast<const bf16x8*>(vg + (int64_t)key * HD + (tid & 15) * 8);
+        for (int j = 0; j < CH; ++j) {
+            const int off = ((k0 + st_row + 16 * j) * HD + st_ch * 8) * 2;
+            rk[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+            rv[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
         }
     };
     auto lstore = [&](int buf) {
+        bf16* dk = sK + buf * K_ELEMS + st_row * KP + st_ch * 8;
+        bf16* dv = sV + buf * V_ELEMS + st_row * VP + st_ch * 8;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tid + 256 * j;
-            *reinterpret_cast<bf16x8*>(&sK[buf][k_off(c >> 4, c & 15)]) = rk[j];
-        }
-        const int cell = tid >> 4, dc = tid & 15;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 v4 = {rv[0][e], rv[1][e], rv[2][e], rv[3][e]};
-            *reinterpret_cast<bf16x4*>(&sV[buf][vt_off(dc * 8 + e, cell)]) = v4;
+        for (int j = 0; j < CH; ++j) {
+            *reinterpret_cast<int4v*>(dk + 16 * j * KP) = rk[j];
+            *reinterpret_cast<int4v*>(dv + 16 * j * VP) = rv[j];
         }
     };
+    // K fragment (A of S^T = K Q^T): row kb*32 + lane%32, 16-byte chunk 2s + lane/32.
+    const int k_rd = (lane & 31) * KP + (lane >> 5) * 8;
+    // V^T fragment (A of O^T = V^T P^T) by transpose reads.  In the score accumulator, element j
+    // of lane half q = lane/32 is key 8(j/4) + 4q + j%4 of its 16-key step.  Lane i' of 16-lane
+    // group G reads row 4(G/2) + i'/4 (and +8), columns 16(G%2) + 4(i'%4): after the transpose
+    // lane l holds rows 4q + 0..3 (and 8 + 4q + 0..3) of column l%32 - the same keys.
+    const int G = lane >> 4, ip = lane & 15;
+    const int v_rd = (4 * (G >> 1) + (ip >> 2)) * VP + 16 * (G & 1) + 4 * (ip & 3);
 
     f32x16 o[4];
 #pragma unroll
@@ -109,14 +130,18 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(AttnArgs a, float sc
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
     float m_run = -1e30f, l_run = 0.f;
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
     gload(0);
     lstore(0);
+    __builtin_amdgcn_s_waitcnt(0);   // Q fragments resident: no loop-carried waits on them
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < ntiles) gload(kt + 1);
+        if (kt + 1 < ntiles) gload((kt + 1) * KT);
         const int k0 = kt * KT;
+        const bf16* sKb = sK + buf * K_ELEMS + k_rd;
+        const bf16* sVb = sV + buf * V_ELEMS + v_rd;
 
         // ---- S^T for the two 32-key blocks of the tile
         f32x16 sacc[2];
@@ -124,15 +149,17 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(AttnArgs a, float sc
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             live[kb] = (k0 + kb * 32) <= wave_last;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
             if (live[kb]) {
+                const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-                        &sK[buf][k_off(kb * 32 + (lane & 31), 2 * s + (lane >> 5))]);
+                for (int s = 1; s < 8; ++s) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP + s * 16);
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
                 }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = -INFINITY;
             }
         }
         // ---- causal mask (only tiles reaching past the wave's first query)
@@ -142,49 +169,52 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(AttnArgs a, float sc
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (!live[kb] || key > my_pos) sacc[kb][r] = -INFINITY;
+                    if (key > my_pos) sacc[kb][r] = -INFINITY;
                 }
         }
-        // ---- online softmax in base 2
+        // ---- online softmax in base 2 with a lazily updated reference max
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt * scale_log2);
-        const float corr = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= corr;
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+        if (__any(mt > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float corr = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= corr;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= corr;
-
+                for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+        }
         bf16x8 pf[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float pv = fast_exp2(fmaf(sacc[kb][8 * hf + j], scale_log2, -m_new));
-                    l_run += pv;
-                    pf[kb][hf][j] = (bf16)pv;
+                for (int j = 0; j < 8; ++j)
+                    pf[kb][hf][j] = (bf16)fast_exp2(fmaf(sacc[kb][8 * hf + j], scale_log2, -m_run));
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const bf16x2 pp = {pf[kb][hf][j], pf[kb][hf][j + 1]};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
                 }
+            }
 
-        // ---- O^T += V^T P^T ; key of element j of lane group q: 16hf + 8(j/4) + 4q + j%4
+        // ---- O^T += V^T P^T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (!live[kb]) continue;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const int cell0 = kb * 8 + hf * 4 + (lane >> 5);
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const int d = db * 32 + (lane & 31);
-                    const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(&sV[buf][vt_off(d, cell0)]);
-                    const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(&sV[buf][vt_off(d, cell0 + 2)]);
+                    const bf16* p = sVb + (kb * 32 + hf * 16) * VP + db * 32;
+                    const bf16x4 v0 = lds_read_tr(p);
+                    const bf16x4 v1 = lds_read_tr(p + 8 * VP);
                     const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hf], o[db], 0, 0, 0);
                 }
@@ -222,11 +252,11 @@ hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) 
     const int qb = 32 * (4 / hpw);
     const dim3 grid((unsigned)((a.T + qb - 1) / qb), (unsigned)(a.Hkv * (g / hpw)), (unsigned)a.B);
     if (hpw == 4)
-        flash_prefill_kernel<4><<<grid, 256, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<4><<<grid, NT, 0, stream>>>(a, scale_log2);
     else if (hpw == 2)
-        flash_prefill_kernel<2><<<grid, 256, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<2><<<grid, NT, 0, stream>>>(a, scale_log2);
     else
-        flash_prefill_kernel<1><<<grid, 256, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<1><<<grid, NT, 0, stream>>>(a, scale_log2);
     return hipGetLastError();
 }
 

@@ -145,6 +145,8 @@ qwen3_status check_sizes(const qwen3_layer* L, int32_t batch, int32_t seq_len, i
         return fail(QWEN3_ERR_UNSUPPORTED, "batch*seq_len too large for 32-bit activation indexing");
     if ((int64_t)batch * c.num_key_value_heads * std::max(cap, seq_len) * c.head_dim >= (int64_t)1 << 40)
         return fail(QWEN3_ERR_UNSUPPORTED, "cache too large");
+    if (((int64_t)std::max(cap, seq_len) + 64) * c.head_dim * 4 >= (int64_t)1 << 31)
+        return fail(QWEN3_ERR_UNSUPPORTED, "cache_capacity too large for 32-bit per-sequence offsets");
     return QWEN3_OK;
 }
 
