@@ -6,11 +6,14 @@
 // weights [out, in], no bias.  Both operands are therefore K-contiguous, which is exactly the
 // per-lane operand layout of v_mfma_f32_32x32x16_bf16 (each lane feeds 8 consecutive k).
 //
-// Large-M kernel: 128x128 output tile per 256-thread workgroup, 4 waves in a 2x2 grid each
-// owning a 64x64 sub-tile (2x2 MFMA 32x32 blocks), BK = 64, two LDS stages; the next k-slab is
-// fetched into registers while the current one feeds the MFMAs.  LDS rows are 128 bytes; the
-// 16-byte chunk index is XOR-swizzled with the row so that the 8 lanes served per LDS cycle hit
-// distinct banks both when storing and when reading operand fragments.
+// Large-M kernel, templated on the workgroup tile BM x BN and its WM x WN wave grid (each wave
+// owns (BM/WM) x (BN/WN), i.e. FM x FN blocks of 32x32); BK = 64, two LDS stages, the next
+// k-slab fetched into registers while the current one feeds the MFMAs.  LDS rows are padded to
+// 144 bytes: the 16 lanes served per cycle by the 64-bank LDS then read 16 rows of the same
+// 16-byte chunk from 16 disjoint bank groups, and every fragment address is a per-lane base
+// plus an immediate.  Large problems use 256x256 tiles on 8 waves (one workgroup per CU, two
+// waves per SIMD, half the L2 traffic per FLOP of 128x128); smaller ones 128x128 on 4 waves,
+// and problems with fewer than 256 such tiles 64x64 (64x128 for SwiGLU) so every CU has work.
 // Tiles are remapped so that each XCD works on a contiguous band of tiles, grouped 8 M-tiles
 // at a time for L2 reuse of the weight tiles.
 //
@@ -24,7 +27,8 @@ namespace q3 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
+constexpr int LP = BK + 8;   // LDS row pitch in elements (144 bytes)
 constexpr int kGroupM = 8;
 
 struct DevGemm {
@@ -57,16 +61,20 @@ __device__ __forceinline__ void epilogue_store(const DevGemm& p, int row, int co
     }
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row & 7)) << 3); }
-
-template <Epilogue EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(DevGemm p) {
+template <Epilogue EPI, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
-    __shared__ __attribute__((aligned(16))) bf16 sA[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * BK];
+    constexpr int NT = WM * WN * 64;
+    constexpr int TM = BM / WM, TN = BN / WN;        // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32;        // 32x32 blocks per wave
+    constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;  // 16-byte chunks staged per thread per slab
+    static_assert(CA >= 1 && CB >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile vs threads");
+    static_assert(!DUAL || TN % 64 == 0, "SwiGLU tiles need whole gate/up block pairs per wave");
+    __shared__ __attribute__((aligned(16))) bf16 sA[2 * BM * LP];
+    __shared__ __attribute__((aligned(16))) bf16 sB[2 * BN * LP];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 
     // ---- tile index: contiguous band per XCD, then grouped along M
     const int total = p.tiles_m * p.tiles_n;
@@ -80,74 +88,77 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(DevGemm p) {
     const int tn = (t % per_group) / gsize;
     const int m0 = tm * BM;
 
-    // ---- global -> register loaders: each thread moves 4 16-byte chunks of A and of B per slab
-    const bf16* ga[4];
-    const bf16* gb[4];
-    int la[4];
+    // ---- global -> register loaders (chunk c = tid + NT j: row c / 8, 16-byte chunk c % 8)
+    const bf16* ga[CA];
+    const bf16* gb[CB];
+    int la[CA], lb[CB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j;
+    for (int j = 0; j < CA; ++j) {
+        const int c = tid + NT * j;
         const int row = c >> 3, ch = c & 7;
-        la[j] = row * BK + swz(row, ch);
+        la[j] = row * LP + ch * 8;
         ga[j] = p.a + (int64_t)min(m0 + row, p.M - 1) * p.K + ch * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        const int c = tid + NT * j;
+        const int row = c >> 3, ch = c & 7;
+        lb[j] = row * LP + ch * 8;
         if constexpr (DUAL) {
-            // tile rows in blocks of 32: gate, up, gate, up for output columns tn*64 + [0,32), [32,64)
-            const int n = tn * 64 + (j >> 1) * 32 + (row & 31);
-            gb[j] = p.b[j & 1] + (int64_t)n * p.K + ch * 8;
+            // B tile rows in blocks of 32: gate, up, gate, up, ... of output columns
+            // tn*BN/2 + 32*(row/64) + row%32
+            const int n = tn * (BN / 2) + (row >> 6) * 32 + (row & 31);
+            gb[j] = p.b[(row >> 5) & 1] + (int64_t)n * p.K + ch * 8;
         } else {
             gb[j] = seg_row(p, tn * BN + row) + ch * 8;
         }
     }
-
-    bf16x8 ra[4], rb[4];
+    bf16x8 ra[CA], rb[CB];
     auto gload = [&](int kt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ra[j] = *reinterpret_cast<const bf16x8*>(ga[j] + kt * BK);
-            rb[j] = *reinterpret_cast<const bf16x8*>(gb[j] + kt * BK);
-        }
+        for (int j = 0; j < CA; ++j) ra[j] = *reinterpret_cast<const bf16x8*>(ga[j] + kt * BK);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) rb[j] = *reinterpret_cast<const bf16x8*>(gb[j] + kt * BK);
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<bf16x8*>(&sA[buf][la[j]]) = ra[j];
-            *reinterpret_cast<bf16x8*>(&sB[buf][la[j]]) = rb[j];
-        }
+        for (int j = 0; j < CA; ++j) *reinterpret_cast<bf16x8*>(&sA[buf * BM * LP + la[j]]) = ra[j];
+#pragma unroll
+        for (int j = 0; j < CB; ++j) *reinterpret_cast<bf16x8*>(&sB[buf * BN * LP + lb[j]]) = rb[j];
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // fragment reads: row (wave's first row) + 32 i + lane%32, chunk 2 kk + lane/32
+    const int a_rd = (wm * TM + (lane & 31)) * LP + (lane >> 5) * 8;
+    const int b_rd = (wn * TN + (lane & 31)) * LP + (lane >> 5) * 8;
     const int nk = p.K / BK;
     gload(0);
     lstore(0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) gload(kt + 1);
+        const bf16* pa = sA + buf * BM * LP + a_rd;
+        const bf16* pb = sB + buf * BN * LP + b_rd;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = 2 * kk + (lane >> 5);
-            bf16x8 af[2], bfr[2];
+            bf16x8 af[FM], bfr[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][r * BK + swz(r, ch)]);
-            }
+            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * LP + kk * 16);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = wn * 64 + j * 32 + (lane & 31);
-                bfr[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][r * BK + swz(r, ch)]);
-            }
+            for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(pb + j * 32 * LP + kk * 16);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
         if (kt + 1 < nk) lstore(buf ^ 1);
@@ -157,18 +168,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(DevGemm p) {
     // ---- epilogue.  32x32 accumulator layout: lane l, register r holds
     //      row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its block.
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (row >= p.M) continue;
             if constexpr (DUAL) {
-                const int col = tn * 64 + wn * 32 + (lane & 31);
-                static_cast<bf16*>(p.out)[(int64_t)row * p.N + col] = (bf16)silu_mul(acc[i][0][r], acc[i][1][r]);
+#pragma unroll
+                for (int j = 0; j < FN; j += 2) {   // blocks j (gate) and j+1 (up) share columns
+                    const int col = tn * (BN / 2) + (wn * TN + j * 32) / 2 + (lane & 31);
+                    static_cast<bf16*>(p.out)[(int64_t)row * p.N + col] =
+                        (bf16)silu_mul(acc[i][j][r], acc[i][j + 1][r]);
+                }
             } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = tn * BN + wn * 64 + j * 32 + (lane & 31);
+                for (int j = 0; j < FN; ++j) {
+                    const int col = tn * BN + wn * TN + j * 32 + (lane & 31);
                     epilogue_store<EPI>(p, row, col, acc[i][j][r]);
                 }
             }
@@ -294,20 +309,41 @@ hipError_t launch_gemv_epi(const DevGemm& p, hipStream_t s) {
 
 bool gemm_bf16_supported(int n_rows, int K) { return n_rows % 128 == 0 && K % 128 == 0; }
 
+template <Epilogue EPI, int BM, int BN, int WM, int WN>
+static hipError_t run_tile(DevGemm p, hipStream_t s) {
+    const int bn_out = (EPI == Epilogue::SwiGLU) ? BN / 2 : BN;
+    if (p.N % bn_out || p.K % BK) return hipErrorInvalidValue;
+    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_n = p.N / bn_out;
+    gemm_bf16_kernel<EPI, BM, BN, WM, WN><<<(unsigned)(p.tiles_m * p.tiles_n), WM * WN * 64, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <Epilogue EPI>
+static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
+    // The largest tile that still gives at least one workgroup per CU (256 CUs).
+    constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
+    const int bn256 = DUAL ? 128 : 256, bn128 = DUAL ? 64 : 128;
+    const long tiles256 = (long)((p.M + 255) / 256) * (p.N / bn256);
+    const long tiles128 = (long)((p.M + 127) / 128) * (p.N / bn128);
+    if (tiles256 >= 256 && p.N % bn256 == 0) return run_tile<EPI, 256, 256, 4, 2>(p, s);
+    if (tiles128 >= 256) return run_tile<EPI, 128, 128, 2, 2>(p, s);
+    if constexpr (DUAL)
+        return run_tile<EPI, 64, 128, 2, 2>(p, s);
+    else
+        return run_tile<EPI, 64, 64, 2, 2>(p, s);
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
     if (g.M <= 0) return hipSuccess;
-    DevGemm p = make_dev(g);
-    if (p.K % BK) return hipErrorInvalidValue;
-    p.tiles_m = (p.M + BM - 1) / BM;
-    p.tiles_n = (g.epi == Epilogue::SwiGLU) ? p.N / 64 : p.N / BN;
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    const DevGemm p = make_dev(g);
     switch (g.epi) {
-        case Epilogue::Store: gemm_bf16_kernel<Epilogue::Store><<<grid, 256, 0, s>>>(p); break;
-        case Epilogue::ResidToF32: gemm_bf16_kernel<Epilogue::ResidToF32><<<grid, 256, 0, s>>>(p); break;
-        case Epilogue::SwiGLU: gemm_bf16_kernel<Epilogue::SwiGLU><<<grid, 256, 0, s>>>(p); break;
-        case Epilogue::ResidF32In: gemm_bf16_kernel<Epilogue::ResidF32In><<<grid, 256, 0, s>>>(p); break;
+        case Epilogue::Store: return run_epi<Epilogue::Store>(p, s);
+        case Epilogue::ResidToF32: return run_epi<Epilogue::ResidToF32>(p, s);
+        case Epilogue::SwiGLU: return run_epi<Epilogue::SwiGLU>(p, s);
+        case Epilogue::ResidF32In: return run_epi<Epilogue::ResidF32In>(p, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_bf16(const GemmArgs& g, hipStream_t s) {

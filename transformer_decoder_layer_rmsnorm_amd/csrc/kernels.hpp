@@ -62,8 +62,8 @@ struct QkRopeArgs {
     void* v_cache;          // [B, Hkv, cap, D]
     SeqPositions pos;       // position (and cache slot) of token 0 of each sequence
     int B, T, Hq, Hkv, D, cap;
-    double theta;
     float eps;
+    double turns[64];       // omega_i / (2 pi) for pair i < D/2, omega_i = theta^(-2i/D), fp64
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
 

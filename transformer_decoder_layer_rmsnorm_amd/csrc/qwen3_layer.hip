@@ -56,6 +56,7 @@ struct StageRec {
 struct qwen3_layer {
     qwen3_config cfg;
     qwen3_layer_weights w;
+    double rope_turns[64];   // omega_i / (2 pi), omega_i = theta^(-2i/D), i < D/2
     bool profiling = false;
     std::mutex prof_mu;
     std::vector<std::string> stage_names;
@@ -247,8 +248,8 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     qa.Hkv = Hkv;
     qa.D = D;
     qa.cap = cap;
-    qa.theta = c.rope_theta;
     qa.eps = eps;
+    std::memcpy(qa.turns, L->rope_turns, sizeof(qa.turns));
     STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
     AttnArgs aa{};
     aa.qhat = qhat;
@@ -321,6 +322,12 @@ qwen3_status qwen3_layer_create(const qwen3_config* config, const qwen3_layer_we
     qwen3_layer* L = new qwen3_layer();
     L->cfg = *config;
     L->w = *weights;
+    // RoPE frequencies ("17. A modern architecture: Qwen3", Rotary position embeddings):
+    // omega_i = theta^(-2i/D), kept in fp64 and in turns for the kernel's exact range reduction.
+    for (int i = 0; i < 64; ++i)
+        L->rope_turns[i] = i < config->head_dim / 2
+                               ? std::pow(config->rope_theta, -2.0 * i / config->head_dim) / (2.0 * M_PI)
+                               : 0.0;
     *out_layer = L;
     return QWEN3_OK;
 }
