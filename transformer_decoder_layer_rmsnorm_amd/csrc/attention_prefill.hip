@@ -11,15 +11,23 @@
 // Layout choices for CDNA4:
 //  * A workgroup (4 waves) serves up to 4 query heads of ONE KV head, so each K/V tile staged in
 //    LDS is read by every head of its group (one read of a shared KV head serves g query heads).
-//    Each wave owns 32 queries of one head.  Two workgroups share a CU (<= 256 registers per
-//    lane, 80 KB of LDS each), so one workgroup's softmax overlaps the other's matrix work.
+//    Each wave owns 32 queries of one head.  When the grid would leave CUs idle (short sequences,
+//    g = 2), the two waves of a head pair split every 64-key tile in halves of 32 keys instead of
+//    taking separate queries; their partial (max, sum, O) are merged through LDS at the end.
+//    Two workgroups share a CU (<= 256 registers per lane, 80 KB of LDS each).
+//  * The grid is one-dimensional and ordered so that workgroup L, which the dispatcher places on
+//    XCD L % 8, always serves KV heads of one XCD: a head's K/V (1-4 MB here) stays in that XCD's
+//    L2 instead of being fetched by all eight.  The heaviest query tiles are dispatched first.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: in the 32x32
 //    accumulator a lane holds 16 keys of ONE query (column = lane % 32), so the row max is a
 //    per-lane reduction plus one exchange with lane ^ 32.
+//  * Software pipeline: the scores of tile t+1 are issued to the matrix core before tile t is
+//    exponentiated, so MFMA and VALU work overlap.  K is staged two tiles ahead and V one tile
+//    ahead (two LDS slots each), which needs a single barrier per tile.
 //  * The probabilities stay in registers and feed O^T += V^T P^T directly as the B operand.  V
 //    stays row-major in LDS; its A-operand fragments come from ds_read_b64_tr_b16 transpose reads
 //    whose per-lane row choice reproduces the accumulator's key order (4 consecutive keys from
-//    each lane half, see v_frag below), so no register transpose is needed.
+//    each lane half, see v_rd below), so no register transpose is needed.
 //  * LDS rows are padded (K 272 B, V 320 B) so fragment reads hit all 64 banks once and every
 //    fragment address is a per-lane base plus an immediate.
 //  * K and V tiles are fetched with buffer loads whose descriptor covers exactly the visible
@@ -29,7 +37,7 @@
 //    2^8 and cancels in the final normalisation.  The row sum accumulates the bf16-rounded
 //    probabilities the PV product actually uses (v_dot2), so the weights sum exactly to one.
 //  * Tiles above the diagonal are never visited; per wave, 32-key blocks that lie entirely
-//    above its queries skip their MFMAs.  The heaviest query tiles are dispatched first.
+//    above its queries skip their MFMAs.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -55,25 +63,47 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int HPW>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a,
-                                                                                                   float scale_log2) {
-    constexpr int WPH = 4 / HPW;       // waves per head
-    constexpr int QB = 32 * WPH;       // queries per workgroup
+template <int HPW, int KS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a, float sl2) {
+    constexpr int WPH = 4 / (HPW * KS);
+    constexpr int QB = 32 * WPH;
+    constexpr int NKB = 2 / KS;
+    static_assert(HPW * KS * WPH == 4, "4 waves");
     __shared__ __attribute__((aligned(16))) bf16 sK[2 * K_ELEMS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2 * V_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // wave = (key half ph, query group wq, head hi); ph only varies when KS = 2
+    const int hi = wave % HPW, wq = (wave / HPW) % WPH, ph = wave / (HPW * WPH);
     const int g = a.Hq / a.Hkv;
     const int subs = g / HPW;
-    const int kvh = blockIdx.y / subs;
-    const int h = kvh * g + (blockIdx.y % subs) * HPW + wave / WPH;
-    const int b = blockIdx.z;
     const int nqt = (a.T + QB - 1) / QB;
-    const int q0 = (nqt - 1 - (int)blockIdx.x) * QB;
-    const int qw = q0 + (wave % WPH) * 32;                        // first query index of this wave
+    int kvh, sub, b, qrank;
+    {
+        int r = blockIdx.x;
+        if ((a.Hkv & 7) == 0) {
+            // workgroup L runs on XCD L % 8: give each XCD whole KV heads so their K/V stay in its L2
+            const int xcd = r & 7;
+            r >>= 3;
+            const int hpx = a.Hkv >> 3;
+            const int m = r % hpx; r /= hpx;
+            sub = r % subs; r /= subs;
+            b = r % a.B; r /= a.B;
+            qrank = r;
+            kvh = xcd + 8 * m;
+        } else {
+            kvh = r % a.Hkv; r /= a.Hkv;
+            sub = r % subs; r /= subs;
+            b = r % a.B; r /= a.B;
+            qrank = r;
+        }
+    }
+    const int h = kvh * g + sub * HPW + hi;
+    const int q0 = (nqt - 1 - qrank) * QB;
+    const int qw = q0 + wq * 32;
     const int pos0 = __builtin_amdgcn_readfirstlane(seq_pos(a.pos, b));
-    const int kv_len = pos0 + min(q0 + QB, a.T);                  // keys 0 .. last query position
+    const int kv_len = pos0 + min(q0 + QB, a.T);
     const int ntiles = (kv_len + KT - 1) / KT;
     const int my_pos = pos0 + qw + (lane & 31);
     const int wave_first = pos0 + qw;
@@ -87,7 +117,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + (2 * s + (lane >> 5)) * 8);
     }
-
     // Buffer descriptors over keys 0 .. kv_len-1 of this (sequence, KV head).
     const int64_t kv_base = ((int64_t)b * a.Hkv + kvh) * a.cap * HD;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -97,23 +126,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 
     // Staging: thread moves 16-byte chunk st_ch of keys st_row + 16 j, j < CH.
     const int st_row = tid >> 4, st_ch = tid & 15;
+    const int st_off = (st_row * HD + st_ch * 8) * 2;
     int4v rk[CH], rv[CH];
-    auto gload = [&](int k0) {
+    auto load_k = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int off = ((k0 + st_row + 16 * j) * HD + st_ch * 8) * 2;
-            rk[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-            rv[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-        }
+        for (int j = 0; j < CH; ++j) rk[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, st_off + (t * KT + 16 * j) * HD * 2, 0, 0);
     };
-    auto lstore = [&](int buf) {
-        bf16* dk = sK + buf * K_ELEMS + st_row * KP + st_ch * 8;
-        bf16* dv = sV + buf * V_ELEMS + st_row * VP + st_ch * 8;
+    auto load_v = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            *reinterpret_cast<int4v*>(dk + 16 * j * KP) = rk[j];
-            *reinterpret_cast<int4v*>(dv + 16 * j * VP) = rv[j];
-        }
+        for (int j = 0; j < CH; ++j) rv[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, st_off + (t * KT + 16 * j) * HD * 2, 0, 0);
+    };
+    auto store_k = [&](int slot) {
+        bf16* d = sK + slot * K_ELEMS + st_row * KP + st_ch * 8;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) *reinterpret_cast<int4v*>(d + 16 * j * KP) = rk[j];
+    };
+    auto store_v = [&](int slot) {
+        bf16* d = sV + slot * V_ELEMS + st_row * VP + st_ch * 8;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) *reinterpret_cast<int4v*>(d + 16 * j * VP) = rv[j];
     };
     // K fragment (A of S^T = K Q^T): row kb*32 + lane%32, 16-byte chunk 2s + lane/32.
     const int k_rd = (lane & 31) * KP + (lane >> 5) * 8;
@@ -132,53 +163,45 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     float m_run = -1e30f, l_run = 0.f;
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    gload(0);
-    lstore(0);
-    __builtin_amdgcn_s_waitcnt(0);   // Q fragments resident: no loop-carried waits on them
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < ntiles) gload((kt + 1) * KT);
-        const int k0 = kt * KT;
-        const bf16* sKb = sK + buf * K_ELEMS + k_rd;
-        const bf16* sVb = sV + buf * V_ELEMS + v_rd;
-
-        // ---- S^T for the two 32-key blocks of the tile
-        f32x16 sacc[2];
-        bool live[2];
+    auto s_tile = [&](int t, f32x16 (&sacc)[NKB], bool (&live)[NKB]) {
+        const bf16* sKb = sK + (t & 1) * K_ELEMS + k_rd;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            live[kb] = (k0 + kb * 32) <= wave_last;
-            if (live[kb]) {
+        for (int i = 0; i < NKB; ++i) {
+            const int kb = (KS == 1) ? i : ph;
+            live[i] = (t * KT + kb * 32) <= wave_last;
+            if (live[i]) {
                 const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
+                sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
                 for (int s = 1; s < 8; ++s) {
                     const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP + s * 16);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kb], 0, 0, 0);
+                    sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[i], 0, 0, 0);
                 }
             } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = -INFINITY;
+                for (int r = 0; r < 16; ++r) sacc[i][r] = -INFINITY;
             }
         }
-        // ---- causal mask (only tiles reaching past the wave's first query)
+    };
+    auto softmax_pv = [&](int t, f32x16 (&sacc)[NKB], const bool (&live)[NKB]) {
+        const int k0 = t * KT;
         if (k0 + KT - 1 > wave_first) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int i = 0; i < NKB; ++i) {
+                const int kb = (KS == 1) ? i : ph;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (key > my_pos) sacc[kb][r] = -INFINITY;
+                    if (key > my_pos) sacc[i][r] = -INFINITY;
                 }
+            }
         }
-        // ---- online softmax in base 2 with a lazily updated reference max
         float mt = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < NKB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[i][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
         if (__any(mt > m_run + 8.f)) {
             const float m_new = fmaxf(m_run, mt);
             const float corr = fast_exp2(m_run - m_new);
@@ -189,25 +212,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[db][r] *= corr;
         }
-        bf16x8 pf[2][2];
+        bf16x8 pf[NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < NKB; ++i)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    pf[kb][hf][j] = (bf16)fast_exp2(fmaf(sacc[kb][8 * hf + j], scale_log2, -m_run));
+                for (int j = 0; j < 8; ++j) pf[i][hf][j] = (bf16)fast_exp2(fmaf(sacc[i][8 * hf + j], sl2, -m_run));
 #pragma unroll
                 for (int j = 0; j < 8; j += 2) {
-                    const bf16x2 pp = {pf[kb][hf][j], pf[kb][hf][j + 1]};
+                    const bf16x2 pp = {pf[i][hf][j], pf[i][hf][j + 1]};
                     l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
                 }
             }
-
-        // ---- O^T += V^T P^T
+        const bf16* sVb = sV + (t & 1) * V_ELEMS + v_rd;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (!live[kb]) continue;
+        for (int i = 0; i < NKB; ++i) {
+            if (!live[i]) continue;
+            const int kb = (KS == 1) ? i : ph;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -216,15 +238,67 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
                     const bf16x4 v0 = lds_read_tr(p);
                     const bf16x4 v1 = lds_read_tr(p + 8 * VP);
                     const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hf], o[db], 0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[i][hf], o[db], 0, 0, 0);
                 }
             }
         }
-        if (kt + 1 < ntiles) lstore(buf ^ 1);
+    };
+    // one pipelined step: S of tile t+1 goes out before tile t's softmax and PV
+    auto step = [&](int t, f32x16 (&cur)[NKB], const bool (&lcur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB]) {
+        if (t + 2 < ntiles) load_k(t + 2);
+        if (t + 1 < ntiles) load_v(t + 1);
+        if (t + 1 < ntiles) s_tile(t + 1, nxt, lnxt);
+        softmax_pv(t, cur, lcur);
+        if (t + 2 < ntiles) store_k(t & 1);
+        if (t + 1 < ntiles) store_v((t + 1) & 1);
         __syncthreads();
+    };
+
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (ntiles > 1) {
+        load_k(1);
+        store_k(1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 sa[NKB], sb[NKB];
+    bool la[NKB], lb[NKB];
+    s_tile(0, sa, la);
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, sa, la, sb, lb);
+        if (t + 1 >= ntiles) break;
+        step(t + 1, sb, lb, sa, la);
     }
 
-    // ---- normalise and store: lane holds d = db*32 + 8(r/4) + 4(lane/32) + r%4 of its query
+    if constexpr (KS == 2) {
+        // merge the two key halves: phase-1 waves hand (m, l, O) to phase-0 waves through LDS
+        float* red = reinterpret_cast<float*>(sK);
+        const int slot = hi + HPW * wq;
+        float* mine = red + slot * (66 * 64) + lane;
+        if (ph == 1) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mine[(db * 16 + r) * 64] = o[db][r];
+            mine[64 * 64] = m_run;
+            mine[65 * 64] = l_run;
+        }
+        __syncthreads();
+        if (ph == 1) return;
+        const float m1 = mine[64 * 64], l1 = mine[65 * 64];
+        const float m_new = fmaxf(m_run, m1);
+        const float c0 = fast_exp2(m_run - m_new), c1 = fast_exp2(m1 - m_new);
+        l_run = l_run * c0 + l1 * c1;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * c0 + mine[(db * 16 + r) * 64] * c1;
+    }
+
+    // normalise and store: lane holds d = db*32 + 8(r/4) + 4(lane/32) + r%4 of its query
     const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
     const int q = qw + (lane & 31);
     if (q < a.T) {
@@ -249,14 +323,25 @@ hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) 
     const int g = a.Hq / a.Hkv;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
-    const int qb = 32 * (4 / hpw);
-    const dim3 grid((unsigned)((a.T + qb - 1) / qb), (unsigned)(a.Hkv * (g / hpw)), (unsigned)a.B);
+    // Split tiles between waves (KS = 2) when whole-tile waves would give fewer than two
+    // workgroups per CU.
+    const int64_t wgs_whole = (int64_t)((a.T + 32 * (4 / hpw) - 1) / (32 * (4 / hpw))) * a.Hkv * (g / hpw) * a.B;
+    const bool split = hpw < 4 && wgs_whole < 512;
+    const int ks = split ? 2 : 1;
+    const int qb = 32 * (4 / (hpw * ks));
+    const int64_t wgs = (int64_t)((a.T + qb - 1) / qb) * a.Hkv * (g / hpw) * a.B;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
     if (hpw == 4)
-        flash_prefill_kernel<4><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<4, 1><<<grid, NT, 0, stream>>>(a, scale_log2);
+    else if (hpw == 2 && split)
+        flash_prefill_kernel<2, 2><<<grid, NT, 0, stream>>>(a, scale_log2);
     else if (hpw == 2)
-        flash_prefill_kernel<2><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<2, 1><<<grid, NT, 0, stream>>>(a, scale_log2);
+    else if (split)
+        flash_prefill_kernel<1, 2><<<grid, NT, 0, stream>>>(a, scale_log2);
     else
-        flash_prefill_kernel<1><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<1, 1><<<grid, NT, 0, stream>>>(a, scale_log2);
     return hipGetLastError();
 }
 
