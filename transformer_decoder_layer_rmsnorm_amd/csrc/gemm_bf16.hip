@@ -6,14 +6,20 @@
 // weights [out, in], no bias.  Both operands are therefore K-contiguous, which is exactly the
 // per-lane operand layout of v_mfma_f32_32x32x16_bf16 (each lane feeds 8 consecutive k).
 //
-// Large-M kernel, templated on the workgroup tile BM x BN and its WM x WN wave grid (each wave
-// owns (BM/WM) x (BN/WN), i.e. FM x FN blocks of 32x32); BK = 64, two LDS stages, the next
-// k-slab fetched into registers while the current one feeds the MFMAs.  LDS rows are padded to
-// 144 bytes: the 16 lanes served per cycle by the 64-bank LDS then read 16 rows of the same
-// 16-byte chunk from 16 disjoint bank groups, and every fragment address is a per-lane base
-// plus an immediate.  Large problems use 256x256 tiles on 8 waves (one workgroup per CU, two
-// waves per SIMD, half the L2 traffic per FLOP of 128x128); smaller ones 128x128 on 4 waves,
-// and problems with fewer than 256 such tiles 64x64 (64x128 for SwiGLU) so every CU has work.
+// Large tiles (256 x 256 on 8 waves, one workgroup per CU, two waves per SIMD) stage operands
+// with direct global->LDS loads (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the
+// wave's LDS base + 16 l, without passing through VGPRs), BK = 32 per stage and four stages in
+// flight, so a k-slab is requested three stages before it is used.  LDS rows are unpadded 64-byte
+// rows whose four 16-byte chunks are XOR-swizzled by row, which keeps fragment reads free of bank
+// conflicts; each load instruction covers 16 rows of one operand.
+//
+// Smaller tiles (128 x 128 on 4 waves; 64 x 64, or 64 x 128 for SwiGLU, when fewer than 256
+// tiles would remain) keep a register prefetch: BK = 64, two LDS stages, the next k-slab fetched
+// into registers while the current one feeds the MFMAs, two or more workgroups per CU.  Their LDS
+// rows are padded to 144 bytes: the 16 lanes served per cycle by the 64-bank LDS then read 16 rows
+// of the same 16-byte chunk from 16 disjoint bank groups.
+//
+// Every tile is a grid of 32x32 MFMA blocks per wave (FM x FN blocks of the wave's share).
 // Tiles are remapped so that each XCD works on a contiguous band of tiles, grouped 8 M-tiles
 // at a time for L2 reuse of the weight tiles.
 //
@@ -61,6 +67,49 @@ __device__ __forceinline__ void epilogue_store(const DevGemm& p, int row, int co
     }
 }
 
+// Tile of workgroup `bid`: contiguous band of tiles per XCD (bid % 8), grouped along M.
+__device__ __forceinline__ void tile_of(const DevGemm& p, int bid, int& tm, int& tn) {
+    const int total = p.tiles_m * p.tiles_n;
+    int t = bid;
+    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+    const int per_group = kGroupM * p.tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * kGroupM;
+    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    tm = first_m + (t % per_group) % gsize;
+    tn = (t % per_group) / gsize;
+}
+
+// Epilogue of one wave's FM x FN blocks.  32x32 accumulator layout: lane l, register r holds
+// row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its block.
+template <Epilogue EPI, int BN, int TM, int TN, int FM, int FN>
+__device__ __forceinline__ void write_tile(const DevGemm& p, const f32x16 (&acc)[FM][FN], int m0, int tn, int wm,
+                                           int wn, int lane) {
+    constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (row >= p.M) continue;
+            if constexpr (DUAL) {
+#pragma unroll
+                for (int j = 0; j < FN; j += 2) {   // blocks j (gate) and j+1 (up) share columns
+                    const int col = tn * (BN / 2) + (wn * TN + j * 32) / 2 + (lane & 31);
+                    static_cast<bf16*>(p.out)[(int64_t)row * p.N + col] =
+                        (bf16)silu_mul(acc[i][j][r], acc[i][j + 1][r]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = tn * BN + wn * TN + j * 32 + (lane & 31);
+                    epilogue_store<EPI>(p, row, col, acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
 template <Epilogue EPI, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
@@ -76,16 +125,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
-    // ---- tile index: contiguous band per XCD, then grouped along M
-    const int total = p.tiles_m * p.tiles_n;
-    int t = blockIdx.x;
-    if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-    const int per_group = kGroupM * p.tiles_n;
-    const int group = t / per_group;
-    const int first_m = group * kGroupM;
-    const int gsize = min(p.tiles_m - first_m, kGroupM);
-    const int tm = first_m + (t % per_group) % gsize;
-    const int tn = (t % per_group) / gsize;
+    int tm, tn;
+    tile_of(p, blockIdx.x, tm, tn);
     const int m0 = tm * BM;
 
     // ---- global -> register loaders (chunk c = tid + NT j: row c / 8, 16-byte chunk c % 8)
@@ -165,30 +206,156 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
         __syncthreads();
     }
 
-    // ---- epilogue.  32x32 accumulator layout: lane l, register r holds
-    //      row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its block.
+    write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
+}
+
+// ------------------------------------------------------------------ large tiles, LDS DMA
+constexpr int DBK = 32;   // k per stage: one LDS row = 64 bytes = four 16-byte chunks
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor held in SGPRs: base, stride 0, num_records bytes (reads past them return 0).
+__device__ __forceinline__ int4v sgpr_desc(const void* base, int nbytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    int4v d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffff));
+    d[2] = __builtin_amdgcn_readfirstlane(nbytes);
+    d[3] = 0x00020000;
+    return d;
+}
+// One 16-byte global->LDS load per lane.  Issued as inline assembly so that the compiler does
+// not treat it as an LDS write of unknown extent (it would then wait for every such load before
+// any LDS read, which defeats the multi-stage pipeline); completion is tracked explicitly with
+// vmcnt below.
+__device__ __forceinline__ void dma16(int4v rsrc, int voff, int soff, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr) : "memory");
+}
+// Wait until at most N of this wave's loads are in flight, then barrier.  Also a compiler
+// memory barrier, so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+// Stage data landed when at most `newer` later stages (NI loads each) are still in flight.
+template <int NI, int MAXN>
+__device__ __forceinline__ void wait_stage(int newer) {
+    static_assert(MAXN <= 3 && NI * MAXN < 64, "vmcnt range");
+    if (MAXN >= 3 && newer >= 3) wait_vm_barrier<(MAXN >= 3 ? NI * 3 : 0)>();
+    else if (MAXN >= 2 && newer == 2) wait_vm_barrier<(MAXN >= 2 ? NI * 2 : 0)>();
+    else if (MAXN >= 1 && newer == 1) wait_vm_barrier<NI>();
+    else wait_vm_barrier<0>();
+}
+// Position of 16-byte chunk c of tile row `row` within the LDS row: c ^ chunk_swz(row).  Rows r,
+// r+4, r+8, r+12 (which share banks) get four distinct patterns, and rows r, r+4 differ in the
+// upper bit, so 16 lanes reading one chunk of 16 consecutive rows, or of 8 rows in two adjacent
+// chunks, touch distinct banks.
+__device__ __forceinline__ int chunk_swz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
+
+template <Epilogue EPI, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dma_kernel(DevGemm p) {
+    constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int IA = BM / 16 / NW, IB = BN / 16 / NW;   // load instructions per wave per stage
+    constexpr int NI = IA + IB;
+    static_assert(IA >= 1 && IB >= 1 && (BM / 16) % NW == 0 && (BN / 16) % NW == 0, "tile vs waves");
+    static_assert(!DUAL || TN % 64 == 0, "SwiGLU tiles need whole gate/up block pairs per wave");
+    static_assert(S >= 2 && S <= 5, "stages");
+    constexpr int A_ST = BM * DBK, B_ST = BN * DBK;      // elements per stage
+    __shared__ __attribute__((aligned(1024))) bf16 sA[S * A_ST];
+    __shared__ __attribute__((aligned(1024))) bf16 sB[S * B_ST];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(p, blockIdx.x, tm, tn);
+    const int m0 = tm * BM;
+    const int rowbytes = p.K * 2;
+
+    // Load instruction i of this wave covers tile rows (wave*IA + i)*16 .. +15 of A (resp. B);
+    // lane l moves row +l/4, LDS chunk l%4.  A rows past M read as zeros.
+    int4v ra[IA], rb[IB];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < IA; ++i) {
+        const int r0 = m0 + (wave * IA + i) * 16;
+        const int nrows = max(0, min(16, p.M - r0));
+        ra[i] = sgpr_desc(p.a + (int64_t)min(r0, p.M - 1) * p.K, nrows * rowbytes);
+    }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (row >= p.M) continue;
-            if constexpr (DUAL) {
+    for (int i = 0; i < IB; ++i) {
+        const int lr = (wave * IB + i) * 16;
+        const bf16* base;
+        if constexpr (DUAL) {
+            // B tile rows in blocks of 32: gate, up, gate, up, ... of output columns
+            // tn*BN/2 + 32*(row/64) + row%32
+            const int n = tn * (BN / 2) + (lr >> 6) * 32 + (lr & 31);
+            base = p.b[(lr >> 5) & 1] + (int64_t)n * p.K;
+        } else {
+            base = seg_row(p, tn * BN + lr);   // 16 rows never straddle a segment
+        }
+        rb[i] = sgpr_desc(base, 16 * rowbytes);
+    }
+    const int dma_voff = (lane >> 2) * rowbytes + (((lane & 3) ^ chunk_swz(lane >> 2)) << 4);
+    const unsigned sA_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sA;
+    const unsigned sB_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sB;
+    auto issue = [&](int kt) {
+        const int slot = kt % S;
+        const int soff = kt * (DBK * 2);
 #pragma unroll
-                for (int j = 0; j < FN; j += 2) {   // blocks j (gate) and j+1 (up) share columns
-                    const int col = tn * (BN / 2) + (wn * TN + j * 32) / 2 + (lane & 31);
-                    static_cast<bf16*>(p.out)[(int64_t)row * p.N + col] =
-                        (bf16)silu_mul(acc[i][j][r], acc[i][j + 1][r]);
-                }
-            } else {
+        for (int i = 0; i < IA; ++i)
+            dma16(ra[i], dma_voff, soff,
+                  __builtin_amdgcn_readfirstlane(sA_lds + (slot * A_ST + (wave * IA + i) * 16 * DBK) * 2));
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = tn * BN + wn * TN + j * 32 + (lane & 31);
-                    epilogue_store<EPI>(p, row, col, acc[i][j][r]);
-                }
-            }
+        for (int i = 0; i < IB; ++i)
+            dma16(rb[i], dma_voff, soff,
+                  __builtin_amdgcn_readfirstlane(sB_lds + (slot * B_ST + (wave * IB + i) * 16 * DBK) * 2));
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // fragment reads: row (wave base) + 32 i + lane%32, chunk 2 kk + lane/32 (swizzled)
+    const int fr = lane & 31;
+    const int a_rd0 = (wm * TM + fr) * DBK + (((0 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
+    const int a_rd1 = (wm * TM + fr) * DBK + (((2 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
+    const int b_rd0 = (wn * TN + fr) * DBK + (((0 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
+    const int b_rd1 = (wn * TN + fr) * DBK + (((2 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
+    const int nk = p.K / DBK;
+
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+        if (st < nk) issue(st);
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once at most min(S-2, nk-1-kt) later stages are in flight; the
+        // barrier also retires every wave's reads of slot (kt-1) % S, which is refilled next
+        wait_stage<NI, S - 2>(min(S - 2, nk - 1 - kt));
+        if (kt + S - 1 < nk) issue(kt + S - 1);
+        const bf16* pa = sA + (kt % S) * A_ST;
+        const bf16* pb = sB + (kt % S) * B_ST;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(pa + (kk ? a_rd1 : a_rd0) + i * 32 * DBK);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(pb + (kk ? b_rd1 : b_rd0) + j * 32 * DBK);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     }
+    write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------ skinny (M <= 64)
@@ -319,6 +486,16 @@ static hipError_t run_tile(DevGemm p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <Epilogue EPI, int BM, int BN, int WM, int WN, int S>
+static hipError_t run_dma_tile(DevGemm p, hipStream_t s) {
+    const int bn_out = (EPI == Epilogue::SwiGLU) ? BN / 2 : BN;
+    if (p.N % bn_out || p.K % DBK || (int64_t)p.K * 2 * 16 >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_n = p.N / bn_out;
+    gemm_bf16_dma_kernel<EPI, BM, BN, WM, WN, S><<<(unsigned)(p.tiles_m * p.tiles_n), WM * WN * 64, 0, s>>>(p);
+    return hipGetLastError();
+}
+
 template <Epilogue EPI>
 static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     // The largest tile that still gives at least one workgroup per CU (256 CUs).
@@ -326,7 +503,7 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     const int bn256 = DUAL ? 128 : 256, bn128 = DUAL ? 64 : 128;
     const long tiles256 = (long)((p.M + 255) / 256) * (p.N / bn256);
     const long tiles128 = (long)((p.M + 127) / 128) * (p.N / bn128);
-    if (tiles256 >= 256 && p.N % bn256 == 0) return run_tile<EPI, 256, 256, 4, 2>(p, s);
+    if (tiles256 >= 256 && p.N % bn256 == 0) return run_dma_tile<EPI, 256, 256, 4, 2, 4>(p, s);
     if (tiles128 >= 256) return run_tile<EPI, 128, 128, 2, 2>(p, s);
     if constexpr (DUAL)
         return run_tile<EPI, 64, 128, 2, 2>(p, s);
