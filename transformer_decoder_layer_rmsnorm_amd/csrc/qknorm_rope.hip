@@ -8,11 +8,15 @@
 // paired with feature i + D/2 and the pair is turned by p * omega_i; keys enter the cache
 // already rotated.
 //
-// One 256-thread workgroup per token.  Lane l of a wave owns the rotate-half pair
-// (l, l + D/2), so the rotation needs no data exchange; the pair's cos/sin are computed once
-// per token from an angle formed in fp64 and reused for every head.  The four waves split the
-// Hq + 2 Hkv heads of the token and issue all their loads before processing any head.
-// The frequencies omega_i = theta^(-2i/D) come in fp64 (computed once per layer handle).
+// One 256-thread workgroup per token; the cos/sin of each rotation pair are computed once per
+// token from an angle formed in fp64 (p * omega_i / 2pi, reduced exactly to [-1/2, 1/2] turn,
+// then evaluated in fp32) and reused for every head.  The frequencies omega_i = theta^(-2i/D)
+// come in fp64, computed once per layer handle.
+//
+// bf16, D = 128: 16 lanes per head, four heads per wave instruction.  Lane j of a head owns
+// features 4j..4j+3 and their rotation partners 64+4j..64+4j+3 (8-byte loads and stores, the
+// rotation stays inside the lane) and the head's sum of squares is a 16-lane DPP reduction.
+// Other shapes: lane l of a wave owns the pair (l, l + D/2), one head per wave at a time.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -90,11 +94,113 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
     }
 }
 
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over each 16-lane row of the wave, result in every lane of the row (DPP, no LDS).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of the half row
+    v += dpp_f32<0x140>(v);   // row_mirror: the other half row
+    return v;
+}
+
+__global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
+    constexpr int D = 128;
+    const int tok = blockIdx.x;
+    const int b = tok / a.T;
+    const int t = tok - b * a.T;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slot = lane >> 4;          // head slot within a group of four heads
+    const int j = lane & 15;             // features 4j..4j+3 and 64+4j..64+4j+3
+    const int pos = seq_pos(a.pos, b) + t;
+
+    float cs[4], sn[4], gq[8], gk[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // v_sin_f32 / v_cos_f32 take the angle in turns; the fp64 turn count is reduced
+        // exactly to [-1/2, 1/2] first
+        const double turns = (double)pos * a.turns[4 * j + e];
+        const float r = (float)(turns - rint(turns));
+        sn[e] = __builtin_amdgcn_sinf(r);
+        cs[e] = __builtin_amdgcn_cosf(r);
+    }
+    {
+        const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.q_norm) + 4 * j);
+        const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.q_norm) + 64 + 4 * j);
+        const bf16x4 k0 = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.k_norm) + 4 * j);
+        const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.k_norm) + 64 + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gq[e] = (float)q0[e]; gq[4 + e] = (float)q1[e];
+            gk[e] = (float)k0[e]; gk[4 + e] = (float)k1[e];
+        }
+    }
+
+    const int nheads = a.Hq + 2 * a.Hkv;
+    const int ngroups = (nheads + 3) >> 2;
+    const bf16* src = static_cast<const bf16*>(a.qkv) + (int64_t)tok * nheads * D + 4 * j;
+    bf16* q_dst = static_cast<bf16*>(a.qhat) + ((int64_t)b * a.Hq * a.T + t) * D + 4 * j;
+    bf16* k_dst = static_cast<bf16*>(a.k_cache) + ((int64_t)b * a.Hkv * a.cap + pos) * D + 4 * j;
+    bf16* v_dst = static_cast<bf16*>(a.v_cache) + ((int64_t)b * a.Hkv * a.cap + pos) * D + 4 * j;
+    const int64_t q_stride = (int64_t)a.T * D, kv_stride = (int64_t)a.cap * D;
+
+    // the wave's groups are wave, wave + 4, ...; loads for GB of them are issued first
+    constexpr int GB = 4;
+    for (int g0 = wave; g0 < ngroups; g0 += 4 * GB) {
+        bf16x4 lo[GB], hi[GB];
+#pragma unroll
+        for (int i = 0; i < GB; ++i) {
+            const int h = min(4 * (g0 + 4 * i) + slot, nheads - 1);
+            lo[i] = *reinterpret_cast<const bf16x4*>(src + h * D);
+            hi[i] = *reinterpret_cast<const bf16x4*>(src + h * D + 64);
+        }
+#pragma unroll
+        for (int i = 0; i < GB; ++i) {
+            if (g0 + 4 * i >= ngroups) break;     // uniform across the wave
+            const int h = 4 * (g0 + 4 * i) + slot;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[e] = (float)lo[i][e]; x[4 + e] = (float)hi[i][e]; }
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+            const float rstd = rsqrtf(row16_sum(ss) * (1.0f / D) + a.eps);
+            if (h >= nheads) continue;
+            bf16x4 olo, ohi;
+            bf16* dst;
+            if (h >= a.Hq + a.Hkv) {          // value head: copied to its cache slot unchanged
+                olo = lo[i];
+                ohi = hi[i];
+                dst = v_dst + (h - a.Hq - a.Hkv) * kv_stride;
+            } else {
+                const bool is_q = h < a.Hq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float n0 = (is_q ? gq[e] : gk[e]) * (x[e] * rstd);
+                    const float n1 = (is_q ? gq[4 + e] : gk[4 + e]) * (x[4 + e] * rstd);
+                    olo[e] = (bf16)(n0 * cs[e] - n1 * sn[e]);
+                    ohi[e] = (bf16)(n1 * cs[e] + n0 * sn[e]);
+                }
+                dst = is_q ? q_dst + h * q_stride : k_dst + (h - a.Hq) * kv_stride;
+            }
+            *reinterpret_cast<bf16x4*>(dst) = olo;
+            *reinterpret_cast<bf16x4*>(dst + 64) = ohi;
+        }
+    }
+}
+
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream) {
     const int64_t tokens = (int64_t)args.B * args.T;
     if (tokens <= 0) return hipSuccess;
     if (args.D > 128 || (args.D & 1)) return hipErrorInvalidValue;
-    if (t == DType::BF16)
+    if (t == DType::BF16 && args.D == 128)
+        qknorm_rope_d128_bf16<<<(unsigned)tokens, 256, 0, stream>>>(args);
+    else if (t == DType::BF16)
         qknorm_rope_kernel<bf16><<<(unsigned)tokens, 256, 0, stream>>>(args);
     else
         qknorm_rope_kernel<float><<<(unsigned)tokens, 256, 0, stream>>>(args);
