@@ -10,6 +10,8 @@
 // fully coalesced 1 KB; the per-key dot products are finished with a butterfly over the 16
 // lanes of a key that also splits the g heads across those lanes (log2(g) fewer exchanges).
 // Values are streamed the same way and accumulated per lane for its 8 features.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,31 +23,48 @@ constexpr int HD = 128;
 constexpr int SK = kDecodeSplitKeys;  // keys per workgroup
 constexpr int KPW = SK / 4;           // keys per wave
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Partner exchange within the 16-lane row of a key, step k = 0..3: lane i pairs with i ^ 8
+// (row_ror:8), 7 - i within its half row (row_half_mirror), then i ^ 2 and i ^ 1 (quad
+// permutes).  Each pairing flips lane bit 3, 2, 1, 0 respectively.
+template <int STEP>
+__device__ __forceinline__ float partner(float x) {
+    if constexpr (STEP == 0) return dpp_f32<0x128>(x);
+    else if constexpr (STEP == 1) return dpp_f32<0x141>(x);
+    else if constexpr (STEP == 2) return dpp_f32<0x4E>(x);
+    else return dpp_f32<0xB1>(x);
+}
+
 // Reduce s[0..G) over the 16 lanes sharing a key.  On return s[0] holds the full sum for head
-// `head` (which depends on the lane), every head being held by 16/G of the lanes.
+// `head` (which depends on the lane), every head being held by 16/G of the lanes: at each step
+// a lane keeps one half of its heads and receives its partner's partial sums of that half.
 template <int G>
 __device__ __forceinline__ float key_reduce(float (&s)[G], int lane, int& head) {
-    int n = G;
     head = 0;
+    auto step = [&](auto stepc) {
+        constexpr int STEP = decltype(stepc)::value;
+        constexpr int n = G >> STEP;              // heads still held per lane before this step
+        const bool hi = (lane & (8 >> STEP)) != 0;
+        if constexpr (n > 1) {
+            constexpr int half = n >> 1;
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        if (n > 1) {
-            const bool hi = (lane & off) != 0;
-            const int half = n >> 1;
-#pragma unroll
-            for (int i = 0; i < G / 2; ++i) {
-                if (i < half) {
-                    const float send = hi ? s[i] : s[i + half];
-                    const float keep = hi ? s[i + half] : s[i];
-                    s[i] = keep + __shfl_xor(send, off, 64);
-                }
+            for (int i = 0; i < half; ++i) {
+                const float send = hi ? s[i] : s[i + half];
+                const float keep = hi ? s[i + half] : s[i];
+                s[i] = keep + partner<STEP>(send);
             }
             if (hi) head += half;
-            n = half;
         } else {
-            s[0] += __shfl_xor(s[0], off, 64);
+            s[0] += partner<STEP>(s[0]);
         }
-    }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
     return s[0];
 }
 
@@ -94,6 +113,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
         const float sum = key_reduce<G>(s, lane, head);
         if ((dc & ((16 / G) - 1)) == 0) sP[kk * G + head] = kk < nk ? sum : -INFINITY;
     }
+    // the first value rows are requested now, so HBM stays busy through the softmax phase
+    constexpr int VPRE = 4;
+    bf16x8 vpre[VPRE];
+#pragma unroll
+    for (int i = 0; i < VPRE; ++i)
+        vpre[i] = *reinterpret_cast<const bf16x8*>(vg + (int64_t)min(wave * KPW + 4 * i + ks, nk - 1) * HD);
     __syncthreads();
 
     // ---- per-wave softmax statistics over its 128 keys
@@ -120,17 +145,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < KPW / 4; ++i) {
-        const int kk = wave * KPW + 4 * i + ks;
-        float vv[8];
-        load8(vg + (int64_t)min(kk, nk - 1) * HD, vv);
+    auto accumulate = [&](int kk, const bf16x8& raw) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float pr = sP[kk * G + h];   // 0 for keys beyond the cache
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, vv[e], acc[h][e]);
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr, (float)raw[e], acc[h][e]);
         }
+    };
+#pragma unroll
+    for (int i = 0; i < VPRE; ++i) accumulate(wave * KPW + 4 * i + ks, vpre[i]);
+#pragma unroll 4
+    for (int i = VPRE; i < KPW / 4; ++i) {
+        const int kk = wave * KPW + 4 * i + ks;
+        accumulate(kk, *reinterpret_cast<const bf16x8*>(vg + (int64_t)min(kk, nk - 1) * HD));
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -171,21 +199,63 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
     }
 }
 
-__global__ __launch_bounds__(HD) void decode_combine_kernel(DecodeAttnArgs p) {
+// Merge the splits of one (head, sequence).  The global max of the split maxima comes from a
+// block reduction; then, chunk by chunk, the split weights 2^(m_s - m) go to LDS and the 256
+// threads split the (split, feature) pairs so that each keeps several independent loads in
+// flight; the two halves of the block combine through LDS.
+constexpr int kCombineThreads = 256;
+constexpr int kSplitChunk = 1024;
+
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeAttnArgs p) {
+    __shared__ float sW[kSplitChunk];
+    __shared__ float sRed[kCombineThreads / 64];
+    __shared__ float sO[2][HD];
     const AttnArgs& a = p.a;
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int kv_len = seq_pos(a.pos, b) + 1;
     const int ns = (kv_len + SK - 1) / SK;
     const int64_t row0 = ((int64_t)b * a.Hq + h) * p.splits;
+    const float* ml = p.part_ml + row0 * 2;
+
     float m = -INFINITY;
-    for (int s = 0; s < ns; ++s) m = fmaxf(m, p.part_ml[(row0 + s) * 2]);
-    float l = 0.f, o = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(p.part_ml[(row0 + s) * 2] - m);
-        l += p.part_ml[(row0 + s) * 2 + 1] * w;
-        o += p.part_o[(row0 + s) * HD + d] * w;
+    for (int s = tid; s < ns; s += kCombineThreads) m = fmaxf(m, ml[2 * s]);
+    m = wave_max(m);
+    if (lane == 0) sRed[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+
+    // thread (half, d) sums splits half, half + 2, ... of each chunk for feature d
+    const int d = tid & (HD - 1), half = tid >> 7;
+    const float* po = p.part_o + row0 * HD + d;
+    float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int c0 = 0; c0 < ns; c0 += kSplitChunk) {
+        const int n = min(kSplitChunk, ns - c0);
+        __syncthreads();                        // previous chunk's weights are no longer read
+        for (int s = tid; s < n; s += kCombineThreads) {
+            const float w = fast_exp2(ml[2 * (c0 + s)] - m);
+            sW[s] = w;
+            l = fmaf(w, ml[2 * (c0 + s) + 1], l);
+        }
+        __syncthreads();
+        const float* pc = po + (int64_t)c0 * HD;
+        int s = half;
+        for (; s + 6 < n; s += 8) {
+            o0 = fmaf(pc[(int64_t)s * HD], sW[s], o0);
+            o1 = fmaf(pc[(int64_t)(s + 2) * HD], sW[s + 2], o1);
+            o2 = fmaf(pc[(int64_t)(s + 4) * HD], sW[s + 4], o2);
+            o3 = fmaf(pc[(int64_t)(s + 6) * HD], sW[s + 6], o3);
+        }
+        for (; s < n; s += 2) o0 = fmaf(pc[(int64_t)s * HD], sW[s], o0);
     }
-    static_cast<bf16*>(a.out)[(int64_t)b * a.Hq * HD + (int64_t)h * HD + d] = (bf16)(o / l);
+    l = wave_sum(l);
+    __syncthreads();
+    if (lane == 0) sRed[wave] = l;
+    sO[half][d] = (o0 + o1) + (o2 + o3);
+    __syncthreads();
+    l = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+    if (half == 0)
+        static_cast<bf16*>(a.out)[(int64_t)b * a.Hq * HD + (int64_t)h * HD + d] = (bf16)((sO[0][d] + sO[1][d]) / l);
 }
 
 template <int G>
@@ -215,7 +285,7 @@ hipError_t launch_attention_decode_combine_bf16(const DecodeAttnArgs& p, hipStre
     const AttnArgs& a = p.a;
     if (a.D != HD || a.T != 1) return hipErrorInvalidValue;
     if (a.B <= 0) return hipSuccess;
-    decode_combine_kernel<<<dim3((unsigned)a.Hq, (unsigned)a.B), HD, 0, stream>>>(p);
+    decode_combine_kernel<<<dim3((unsigned)a.Hq, (unsigned)a.B), kCombineThreads, 0, stream>>>(p);
     return hipGetLastError();
 }
 
