@@ -159,6 +159,28 @@ def cpu_baseline(si, wl, min_s=10.0, budget_s=30.0):
                       f"(B{wl.batch} x T{wl.seq_len}), {el:.1f} s"}
 
 
+def measured_traffic(kernel, workload):
+    """HBM traffic per launch recorded by the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (profiles/roofline_traffic.json, counters scaled by the copy calibration), or None when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, "profiles", "roofline_traffic.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for e in rec.get("entries", []):
+        if e.get("kernel") == kernel and e.get("workload") == workload:
+            try:
+                with open(os.path.join(here, e["source"]), "rb") as f:
+                    sha = hashlib.sha256(f.read()).hexdigest()
+            except OSError:
+                return None
+            return e["traffic_bytes"] if sha == e.get("source_sha256") else None
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,7 +237,7 @@ def main():
                    "head_dim": wl.cfg.head_dim, "intermediate_size": wl.cfg.intermediate_size},
         "roofline": {"bound": "mfma", "kernel": res["dominant"], "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(res["dominant"], wl.name)},
         "layer_tflops": round(res["layer_tflops"], 1),
         "layer_frac_of_bf16_peak": round(res["layer_tflops"] / PEAK_BF16_TFLOPS, 4),
         "kernels": res["kernels"],
@@ -235,7 +257,7 @@ def main():
             "tokens_per_s": round(r5["tokens_per_s"], 1), "ms_per_step": round(r5["ms_per_step"], 4),
             "roofline": {"bound": "hbm", "kernel": "attention_decode_split", "achieved": round(r5["attention_gbs"], 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r5["attention_frac_of_hbm_peak"], 4),
-                         "traffic": None},
+                         "traffic": measured_traffic("attention_decode_split", wl5.name)},
             "kernels": r5["kernels"]}
     if calib:
         line["copy_calibration"] = calib
