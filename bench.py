@@ -6,8 +6,9 @@ GQA causal attention, o_proj + residual, RMSNorm, gate/up + SwiGLU, down + resid
 Prints ONE JSON line: tokens/s of that step, the roofline fraction of its dominant kernel
 (per-kernel durations from HIP events recorded by the library around each launch, on the
 launch stream), the float64 CPU oracle timed on a bounded sample of the same workload, and,
-as extra context, the 8B-shaped layer prefill (B1 T8192) and the 8B-shaped decode step on a
-32768-key cache (decode attention achieved GB/s against HBM peak).
+as extra context, the 8B-shaped layer prefill (B1 T8192), the 28-layer 0.6B-shaped stack with its
+final norm (B4 T4096) and the 8B-shaped decode step on a 32768-key cache (decode attention
+achieved GB/s against HBM peak).
 """
 from __future__ import annotations
 
@@ -134,6 +135,44 @@ def bench_decode(torch, si, nat, wl, steps, warmup, device):
                 kernels={k: {"avg_ms": round(v, 5)} for k, v in avg.items()})
 
 
+def bench_stack(torch, si, nat, wl, steps, warmup, device):
+    """The layer stack with its final RMSNorm: one step runs every layer's prefill in turn, each
+    with its own random-init weights and K/V cache, then the final norm (one shared workspace,
+    one stream)."""
+    cfg = wl.cfg
+    dt = torch.bfloat16
+    g = torch.Generator(device=device).manual_seed(wl.seed)
+    layers, caches = [], []
+    for _ in range(wl.layers):
+        w = {}
+        for name, shape in si.weight_shapes(cfg).items():
+            z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+            w[name] = ((1 + 0.1 * z) if name in si.GAIN_NAMES else 0.02 * z).to(dt)
+        layers.append((nat.Layer(cfg, w), w))
+        kc = torch.zeros((wl.batch, cfg.num_key_value_heads, wl.seq_len, cfg.head_dim), dtype=dt, device=device)
+        caches.append((kc, torch.zeros_like(kc)))
+    gain = (1 + 0.1 * torch.randn(cfg.hidden_size, generator=g, device=device)).to(dt)
+    x = torch.randn((wl.batch, wl.seq_len, cfg.hidden_size), generator=g, device=device).to(dt)
+    bufs = (torch.empty_like(x), torch.empty_like(x))
+    out = torch.empty_like(x)
+    ws = torch.empty(layers[0][0].workspace_size(wl.batch, wl.seq_len, wl.seq_len), dtype=torch.uint8, device=device)
+
+    def run():
+        cur = x
+        for i, ((layer, _), (kc, vc)) in enumerate(zip(layers, caches)):
+            nxt = bufs[i & 1]
+            layer.prefill(cur, nxt, kc, vc, ws)
+            cur = nxt
+        nat.rmsnorm(cur, gain, out, cfg.rms_norm_eps)
+
+    ms = time_steps(torch, run, steps, warmup)
+    flops = sum(layer_flops(cfg, wl.batch, wl.seq_len).values()) * wl.layers
+    for layer, _ in layers:
+        layer.close()
+    return dict(ms_per_step=ms, tokens_per_s=wl.batch * wl.seq_len / (ms * 1e-3),
+                ms_per_layer=ms / wl.layers, stack_tflops=flops / (ms * 1e-3) / 1e12)
+
+
 def cpu_baseline(si, wl, min_s=10.0, budget_s=30.0):
     """The float64 oracle, untuned, on a bounded sample of the same workload."""
     import oracle
@@ -187,7 +226,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 8B prefill and 32K decode measurements")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 8B prefill, 28-layer stack and 32K decode measurements")
     ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of the 8B prefill / decode runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
@@ -250,6 +289,13 @@ def main():
             "tokens_per_s": round(r4["tokens_per_s"], 1), "ms_per_step": round(r4["ms_per_step"], 4),
             "layer_tflops": round(r4["layer_tflops"], 1),
             "layer_frac_of_bf16_peak": round(r4["layer_tflops"] / PEAK_BF16_TFLOPS, 4), "kernels": r4["kernels"]}
+        wl3 = si.WORKLOADS["qwen3-0.6b-stack28-prefill"]
+        print(f"[bench] {wl3.name}", file=sys.stderr, flush=True)
+        r3 = bench_stack(torch, si, nat, wl3, max(2, args.extra_steps // 2), 1, device)
+        line["qwen3_0p6b_stack28_prefill"] = {
+            "tokens_per_s": round(r3["tokens_per_s"], 1), "ms_per_step": round(r3["ms_per_step"], 4),
+            "ms_per_layer": round(r3["ms_per_layer"], 4), "stack_tflops": round(r3["stack_tflops"], 1),
+            "stack_frac_of_bf16_peak": round(r3["stack_tflops"] / PEAK_BF16_TFLOPS, 4)}
         wl5 = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
         print(f"[bench] {wl5.name}", file=sys.stderr, flush=True)
         r5 = bench_decode(torch, si, nat, wl5, 2 * args.extra_steps, 5, device)
