@@ -186,11 +186,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
         const bf16* pa = sA + buf * BM * LP + a_rd;
         const bf16* pb = sB + buf * BN * LP + b_rd;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
+            // With several MFMA blocks per wave the next slab is requested once the first MFMAs
+            // of this one are queued, so a wave that stalls on a full address queue still has
+            // matrix work in flight; with one block per wave it is requested up front.
+            if (kk == (FM * FN >= 4 ? 1 : 0) && kt + 1 < nk) gload(kt + 1);
             bf16x8 af[FM], bfr[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(pa + i * 32 * LP + kk * 16);
@@ -338,7 +341,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dma_kernel(DevGemm p) 
         // stage kt has landed once at most min(S-2, nk-1-kt) later stages are in flight; the
         // barrier also retires every wave's reads of slot (kt-1) % S, which is refilled next
         wait_stage<NI, S - 2>(min(S - 2, nk - 1 - kt));
-        if (kt + S - 1 < nk) issue(kt + S - 1);
         const bf16* pa = sA + (kt % S) * A_ST;
         const bf16* pb = sB + (kt % S) * B_ST;
 #pragma unroll
@@ -353,6 +355,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dma_kernel(DevGemm p) 
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            // the stage S-1 ahead is requested once this stage's first MFMAs are queued: right
+            // after the barrier all waves would hit the address queues at once
+            if (kk == 0 && kt + S - 1 < nk) issue(kt + S - 1);
         }
     }
     write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
