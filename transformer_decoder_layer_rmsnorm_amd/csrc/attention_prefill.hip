@@ -17,7 +17,8 @@
 //    Two workgroups share a CU (<= 256 registers per lane, 80 KB of LDS each).
 //  * The grid is one-dimensional and ordered so that workgroup L, which the dispatcher places on
 //    XCD L % 8, always serves KV heads of one XCD: a head's K/V (1-4 MB here) stays in that XCD's
-//    L2 instead of being fetched by all eight.  The heaviest query tiles are dispatched first.
+//    L2 instead of being fetched by all eight.  The heaviest query tiles are dispatched first;
+//    when the whole grid is resident at once, heavy and light tiles are paired per CU instead.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: in the 32x32
 //    accumulator a lane holds 16 keys of ONE query (column = lane % 32), so the row max is a
 //    per-lane reduction plus one exchange with lane ^ 32.
@@ -64,7 +65,8 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
 }
 
 template <int HPW, int KS>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a, float sl2) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a, float sl2,
+                                                                                                   bool pair_tiles) {
     constexpr int WPH = 4 / (HPW * KS);
     constexpr int QB = 32 * WPH;
     constexpr int NKB = 2 / KS;
@@ -98,6 +100,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
             b = r % a.B; r /= a.B;
             qrank = r;
         }
+    }
+    if (pair_tiles) {
+        // every workgroup is resident at once: the second half of the dispatch order (which
+        // fills each CU's second slot) runs the lightest query tiles first, so a CU pairs query
+        // tile j with tile nqt-1-j and all CUs carry about the same number of key tiles
+        const int half = (nqt + 1) >> 1;
+        if (qrank >= half) qrank = nqt - 1 - (qrank - half);
     }
     const int h = kvh * g + sub * HPW + hi;
     const int q0 = (nqt - 1 - qrank) * QB;
@@ -332,16 +341,17 @@ hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) 
     const int64_t wgs = (int64_t)((a.T + qb - 1) / qb) * a.Hkv * (g / hpw) * a.B;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
+    const bool pair_tiles = wgs <= 512;   // two workgroups per CU on 256 CUs
     if (hpw == 4)
-        flash_prefill_kernel<4, 1><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<4, 1><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else if (hpw == 2 && split)
-        flash_prefill_kernel<2, 2><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<2, 2><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else if (hpw == 2)
-        flash_prefill_kernel<2, 1><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<2, 1><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else if (split)
-        flash_prefill_kernel<1, 2><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<1, 2><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else
-        flash_prefill_kernel<1, 1><<<grid, NT, 0, stream>>>(a, scale_log2);
+        flash_prefill_kernel<1, 1><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     return hipGetLastError();
 }
 
