@@ -111,9 +111,9 @@ qwen3_status qwen3_layer_create(const qwen3_config* config, const qwen3_layer_we
 /* Frees the handle (not the weights).  NULL is ignored. */
 void qwen3_layer_destroy(qwen3_layer* layer);
 
-/* Workspace bytes for a prefill of [batch, seq_len] tokens and for a decode
- * of `batch` tokens over caches of `cache_capacity` slots (pass seq_len = 1
- * for decode only).  Host only. */
+/* Workspace bytes for a prefill of [batch, seq_len] tokens (also onto a
+ * non-empty cache) and for a decode of `batch` tokens over caches of
+ * `cache_capacity` slots (pass seq_len = 1 for decode only).  Host only. */
 qwen3_status qwen3_layer_workspace_size(const qwen3_layer* layer, int32_t batch, int32_t seq_len,
                                         int32_t cache_capacity, size_t* bytes);
 
@@ -132,6 +132,28 @@ qwen3_status qwen3_layer_prefill(qwen3_layer* layer, const void* x, void* y, int
                                  int32_t seq_len, void* k_cache, void* v_cache,
                                  int32_t cache_capacity, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* Prefill onto a non-empty cache (chunked or prefix prefill): x, y are
+ * [batch, seq_len, H]; start_positions is a HOST array [batch] (NULL means all
+ * zero, which is qwen3_layer_prefill).  Sequence b already holds
+ * start_positions[b] rotated keys and values in slots 0..start_positions[b]-1;
+ * its token t sits at position start_positions[b] + t, its khat / v go to that
+ * slot, and it attends keys 0..start_positions[b] + t of its own sequence
+ * ("17. A modern architecture: Qwen3", section The whole model: positions
+ * continue from the cache length; "Transformer architectures: from BERT to
+ * diffusion, lesson 6", section 8: a shared prefix's keys and values are
+ * computed once and reused).  Running a prompt as prefill(T1) followed by
+ * prefill_at(T2, start T1) gives the rows of prefill(T1 + T2).  Up to 64
+ * sequences the start positions travel as launch arguments; for more, they
+ * are copied into the workspace (which must then also cover the `lens` region
+ * of qwen3_layer_workspace_layout).  y may alias x.
+ * Errors: INVALID_ARGUMENT, OUT_OF_RANGE (start_positions[b] < 0,
+ * start_positions[b] + seq_len > cache_capacity or > max_position_embeddings),
+ * WORKSPACE_TOO_SMALL, DEVICE. */
+qwen3_status qwen3_layer_prefill_at(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                    int32_t seq_len, const int32_t* start_positions, void* k_cache,
+                                    void* v_cache, int32_t cache_capacity, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* Decode: one new token per sequence; x, y are [batch, 1, H].  cache_lens is a
  * HOST array [batch]: sequence b already holds cache_lens[b] rotated keys and

@@ -15,7 +15,7 @@ reproduced: the GPU path is judged against the exact result).  Sources:
          Q/K normalization, SwiGLU, The whole model.
   [L6]   "Transformer architectures: from BERT to diffusion, lesson 6"
          (xmarva.github.io), sections 3 Grouped-query attention, 4 Training
-         stability (QK-norm formula), 5 Qwen3 in PyTorch.
+         stability (QK-norm formula), 5 Qwen3 in PyTorch, 8 (prefix caching).
   [CHK]  "Understand modern AI from the inside out" (Qwen3 layer checklist page),
          items on pre-norm order, q_norm/k_norm placement, rotate-half, scaling,
          GQA, causality, SwiGLU and the float32 RMSNorm.
@@ -29,7 +29,7 @@ import numpy as np
 __all__ = [
     "rmsnorm", "rope_inv_freq", "rope_rotate", "silu", "swiglu_mlp",
     "gqa_causal_attention", "qk_norm_rope", "layer_prefill", "layer_prefill_rows",
-    "layer_decode", "stack_prefill",
+    "layer_decode", "layer_prefill_cached", "stack_prefill",
 ]
 
 
@@ -227,6 +227,41 @@ def layer_decode(x, w, cfg, k_cache, v_cache, cache_lens):
         h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_new[b], v_new[b] = khat[:, 0], v[:, 0]
+    return y, khat_new, v_new
+
+
+def layer_prefill_cached(x, w, cfg, k_cache, v_cache, starts):
+    """Prefill of T new tokens per sequence on top of a cache of rotated keys.
+
+    [Q17 The whole model, Qwen3.forward]: without explicit positions the new
+    tokens sit at positions start .. start+T-1, start being the cache length.
+    [Q17 Rotary position embeddings, last paragraph]: cached keys are already
+    rotated and are used as they are; the new tokens rotate their own q and k.
+    [L6 section 8, prefix caching]: a shared prefix's keys and values are
+    computed once and every continuation starts from them.
+    Token t of sequence b (position p = starts[b] + t) attends the cached keys
+    0..starts[b]-1 and the new keys at positions <= p (causal rule).
+    x: [B, T, H]; k_cache, v_cache: per sequence [Hkv, >= start, D] arrays (or a
+    [B, Hkv, cap, D] array); starts: [B] ints.  Returns y [B,T,H], khat_new
+    [B,Hkv,T,D] and v_new [B,Hkv,T,D] (what goes to slots start..start+T-1)."""
+    hsize, hq, hkv, d = _dims(cfg)
+    x = _f64(x)
+    bsz, t = x.shape[0], x.shape[1]
+    y = np.empty_like(x)
+    khat_new = np.empty((bsz, hkv, t, d))
+    v_new = np.empty((bsz, hkv, t, d))
+    for b in range(bsz):
+        p0 = int(starts[b])
+        pos = np.arange(p0, p0 + t, dtype=np.float64)
+        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)          # [T, H]
+        qhat, khat, v = qk_norm_rope(h, w, cfg, pos)                         # [*, T, D]
+        keys = np.concatenate([_f64(k_cache[b])[:, :p0], khat], axis=1)    # [Hkv, p0+T, D]
+        vals = np.concatenate([_f64(v_cache[b])[:, :p0], v], axis=1)
+        attn = gqa_causal_attention(qhat, keys, vals, pos, np.arange(p0 + t, dtype=np.float64))
+        x1 = x[b] + attn.transpose(1, 0, 2).reshape(t, hq * d) @ _f64(w["o_proj"]).T
+        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
+        khat_new[b], v_new[b] = khat, v
     return y, khat_new, v_new
 
 

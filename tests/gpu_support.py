@@ -66,13 +66,13 @@ class GpuLayer:
         n = self.layer.workspace_size(batch, seq_len, cap)
         return torch.empty(n, dtype=torch.uint8, device="cuda")
 
-    def prefill(self, x_dev, cap=None, caches=None, ws=None, y_dev=None):
+    def prefill(self, x_dev, cap=None, caches=None, ws=None, y_dev=None, starts=None):
         b, t, _ = x_dev.shape
         cap = cap or t
         kc, vc = caches or self.alloc_cache(b, cap)
         ws = ws if ws is not None else self.workspace(b, t, cap)
         y = y_dev if y_dev is not None else torch.empty_like(x_dev)
-        self.layer.prefill(x_dev, y, kc, vc, ws)
+        self.layer.prefill(x_dev, y, kc, vc, ws, start_positions=starts)
         torch.cuda.synchronize()
         return y, kc, vc, ws
 

@@ -146,6 +146,28 @@ def test_decode_validation_before_launch(layer):
         == nat.QWEN3_ERR_INVALID_ARGUMENT
 
 
+def prefill_at(layer, starts, t=4, cap=16, ws_bytes=1 << 30):
+    arr = None if starts is None else (ctypes.c_int32 * len(starts))(*starts)
+    b = 1 if starts is None else len(starts)
+    return nat.lib().qwen3_layer_prefill_at(layer, FAKE, FAKE, b, t, arr, FAKE, FAKE, cap, FAKE, ws_bytes, None)
+
+
+def test_prefill_at_validation_before_launch(layer):
+    assert prefill_at(layer, [0, -1]) == nat.QWEN3_ERR_OUT_OF_RANGE           # negative start
+    assert prefill_at(layer, [12, 13]) == nat.QWEN3_ERR_OUT_OF_RANGE          # 13 + 4 > capacity 16
+    assert prefill_at(layer, [40958], cap=50000) == nat.QWEN3_ERR_OUT_OF_RANGE  # passes the position limit
+    assert prefill_at(layer, [3, 4], ws_bytes=100) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+    # more than 64 sequences with starts: the positions need the workspace's `lens` region too
+    lay = nat.WorkspaceLayout()
+    assert nat.lib().qwen3_layer_workspace_layout(layer, 65, 4, 0, ctypes.byref(lay)) == nat.QWEN3_OK
+    assert prefill_at(layer, [1] * 65, ws_bytes=lay.lens) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+    size = ctypes.c_size_t()
+    assert nat.lib().qwen3_layer_workspace_size(layer, 65, 4, 0, ctypes.byref(size)) == nat.QWEN3_OK
+    assert size.value >= lay.lens + 65 * 4
+    assert nat.lib().qwen3_layer_prefill_at(layer, None, FAKE, 1, 4, None, FAKE, FAKE, 16, FAKE, 1 << 30, None) \
+        == nat.QWEN3_ERR_INVALID_ARGUMENT
+
+
 def test_rmsnorm_validation_and_status_strings():
     L = nat.lib()
     assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 4, 12, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_UNSUPPORTED

@@ -196,6 +196,92 @@ def test_bf16_decode_continues_prefill():
     assert_bf16_parity(to_np(y)[0, 0], to_np(yfull)[0, t - 1], "decode row vs prefill row")
 
 
+def _random_cache(cfg, starts, cap, seed):
+    b, hkv = len(starts), cfg.num_key_value_heads
+    kc = np.zeros((b, hkv, cap, cfg.head_dim), np.float32)
+    vc = np.zeros((b, hkv, cap, cfg.head_dim), np.float32)
+    for i, n in enumerate(starts):
+        for h in range(hkv):
+            kc[i, h, :n] = si.cache_block(cfg, "k", i, h, n, seed=seed)
+            vc[i, h, :n] = si.cache_block(cfg, "v", i, h, n, seed=seed)
+    return kc, vc
+
+
+@pytest.mark.parametrize("hq,hkv,t", [(4, 2, 77), (8, 1, 33), (8, 8, 130)])
+def test_bf16_prefill_at_matches_oracle_ragged(hq, hkv, t):
+    # prefill onto caches already holding 0, 1, 63, 64, 65, 200 and 511 keys
+    cfg = small_bf16_cfg(hq=hq, hkv=hkv)
+    gl = GpuLayer.seeded(cfg, seed=21)
+    starts = [0, 1, 63, 64, 65, 200, 511]
+    b = len(starts)
+    cap = max(starts) + t + 5
+    log(f"bf16 prefill_at Hq{hq} Hkv{hkv} T{t} starts {starts}")
+    kc, vc = _random_cache(cfg, starts, cap, seed=21)
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    x = si.layer_input(cfg, b, t, seed=21)
+    y, kd, vd, _ = gl.prefill(to_dev(x, cfg), cap=cap, caches=(kd, vd), starts=starts)
+    ref, knew, vnew = oracle.layer_prefill_cached(x, gl.w_np, cfg, kc, vc, starts)
+    assert_bf16_parity(to_np(y), ref, "prefill_at y")
+    kg, vg = to_np(kd), to_np(vd)
+    for i, n in enumerate(starts):
+        # slots before the start and after the new tokens are untouched
+        assert np.array_equal(kg[i, :, :n], kc[i, :, :n]) and np.array_equal(vg[i, :, :n], vc[i, :, :n])
+        assert not kg[i, :, n + t:].any() and not vg[i, :, n + t:].any()
+        assert_bf16_parity(kg[i, :, n:n + t], knew[i], f"new keys of sequence {i}")
+        assert_bf16_parity(vg[i, :, n:n + t], vnew[i], f"new values of sequence {i}")
+
+
+def test_bf16_chunked_prefill_equals_one_shot():
+    cfg = small_bf16_cfg()
+    gl = GpuLayer.seeded(cfg, seed=22)
+    t1, t2 = 150, 97
+    x = si.layer_input(cfg, 2, t1 + t2, seed=22)
+    log(f"bf16 chunked prefill {t1} + {t2}")
+    yfull, *_ = gl.prefill(to_dev(x, cfg))
+    cap = t1 + t2
+    kc, vc = gl.alloc_cache(2, cap)
+    y1, *_ = gl.prefill(to_dev(x[:, :t1], cfg), caches=(kc, vc), cap=cap)
+    y2, *_ = gl.prefill(to_dev(x[:, t1:], cfg), caches=(kc, vc), cap=cap, starts=[t1, t1])
+    got = np.concatenate([to_np(y1), to_np(y2)], axis=1)
+    assert_bf16_parity(got, to_np(yfull), "chunked vs one-shot")
+    rows = [(0, t1), (1, t1 + t2 - 1), (0, t1 + 40), (1, 3)]
+    ref = oracle.layer_prefill_rows(x, gl.w_np, cfg, rows)
+    for n, (b, r) in enumerate(rows):
+        assert_bf16_parity(got[b, r], ref[n], f"chunked row {(b, r)} vs oracle")
+
+
+def test_bf16_prefill_at_many_sequences_positions_in_workspace():
+    # more than 64 sequences: the start positions go through the workspace
+    cfg = small_bf16_cfg()
+    gl = GpuLayer.seeded(cfg, seed=23)
+    starts = [(5 * i) % 37 for i in range(66)]
+    t = 3
+    cap = max(starts) + t
+    log(f"bf16 prefill_at {len(starts)} sequences")
+    kc, vc = _random_cache(cfg, starts, cap, seed=23)
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    x = si.layer_input(cfg, len(starts), t, seed=23)
+    y, *_ = gl.prefill(to_dev(x, cfg), cap=cap, caches=(kd, vd), starts=starts)
+    ref, _, _ = oracle.layer_prefill_cached(x, gl.w_np, cfg, kc, vc, starts)
+    assert_bf16_parity(to_np(y), ref, "prefill_at y, 66 sequences")
+
+
+def test_f32_prefill_at_matches_oracle():
+    cfg = si.TINY_F32
+    gl = GpuLayer.seeded(cfg, seed=24)
+    starts = [0, 5, 16]
+    t = 7
+    cap = max(starts) + t
+    log("f32 prefill_at")
+    kc, vc = _random_cache(cfg, starts, cap, seed=24)
+    x = si.layer_input(cfg, len(starts), t, seed=24)
+    y, kd, vd, _ = gl.prefill(to_dev(x, cfg), cap=cap, caches=(to_dev(kc, cfg), to_dev(vc, cfg)), starts=starts)
+    ref, knew, _ = oracle.layer_prefill_cached(x, gl.w_np, cfg, kc, vc, starts)
+    assert_f32_parity(to_np(y), ref, "f32 prefill_at y")
+    for i, n in enumerate(starts):
+        assert_f32_parity(to_np(kd)[i, :, n:n + t], knew[i], f"f32 new keys {i}")
+
+
 def test_profiling_reports_every_stage():
     cfg = small_bf16_cfg()
     gl = GpuLayer.seeded(cfg, seed=19)

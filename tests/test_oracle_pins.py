@@ -346,6 +346,71 @@ def test_decode_continues_prefill():
         np.testing.assert_allclose(vnew[b], full["v"][b, :, n], atol=1e-12)
 
 
+def test_cached_prefill_continues_prefill():
+    # prefill(n) then the remaining tokens as a prefill onto that cache == the rows n.. of
+    # prefill(n + T) (causal rule + positions continuing from the cache length), ragged n
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=18)
+    x = si.layer_input(cfg, 3, 13, seed=18)
+    t_new = 5
+    starts = [8, 0, 3]
+    cap = 16
+    kc = np.zeros((3, 2, cap, 32))
+    vc = np.zeros((3, 2, cap, 32))
+    xin = np.zeros((3, t_new, 64), dtype=x.dtype)
+    for b, n in enumerate(starts):
+        if n:
+            pre = oracle.layer_prefill(x[b:b + 1, :n], w, cfg)
+            kc[b, :, :n] = pre["khat"][0]
+            vc[b, :, :n] = pre["v"][0]
+        xin[b] = x[b, n:n + t_new]
+    y, knew, vnew = oracle.layer_prefill_cached(xin, w, cfg, kc, vc, starts)
+    for b, n in enumerate(starts):
+        full = oracle.layer_prefill(x[b:b + 1, :n + t_new], w, cfg)
+        np.testing.assert_allclose(y[b], full["y"][0, n:], atol=1e-12)
+        np.testing.assert_allclose(knew[b], full["khat"][0, :, n:], atol=1e-12)
+        np.testing.assert_allclose(vnew[b], full["v"][0, :, n:], atol=1e-12)
+
+
+def test_cached_prefill_matches_library_assembly_on_given_cache():
+    # arbitrary cached keys/values (not produced by this layer) are used as they are; the new
+    # tokens rotate at positions start.. and see the cache plus their own causal prefix
+    cfg = tiny_cfg()
+    hs, hq, hkv, d, eps = 64, 4, 2, 32, cfg.rms_norm_eps
+    w = si.layer_weights(cfg, seed=19)
+    x = si.layer_input(cfg, 1, 6, seed=19)
+    p0 = 9
+    rng = np.random.default_rng(19)
+    kc = rng.standard_normal((1, hkv, 20, d))
+    vc = rng.standard_normal((1, hkv, 20, d))
+    y, _, _ = oracle.layer_prefill_cached(x, w, cfg, kc, vc, [p0])
+
+    t64 = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    X = t64(x)
+    t = X.shape[1]
+    H = F.rms_norm(X, (hs,), t64(w["input_layernorm"]), eps)
+    q = F.rms_norm(F.linear(H, t64(w["q_proj"])).view(1, t, hq, d), (d,), t64(w["q_norm"]), eps).transpose(1, 2)
+    k = F.rms_norm(F.linear(H, t64(w["k_proj"])).view(1, t, hkv, d), (d,), t64(w["k_norm"]), eps).transpose(1, 2)
+    v = F.linear(H, t64(w["v_proj"])).view(1, t, hkv, d).transpose(1, 2)
+    inv = torch.tensor([cfg.rope_theta ** (-2.0 * i / d) for i in range(d // 2)], dtype=torch.float64)
+    pos = torch.arange(p0, p0 + t, dtype=torch.float64)
+    rot = torch.polar(torch.ones(t, d // 2, dtype=torch.float64), pos[:, None] * inv[None, :])
+
+    def rope(a):
+        z = torch.complex(a[..., : d // 2], a[..., d // 2:]) * rot
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    keys = torch.cat([t64(kc[:, :, :p0]), rope(k)], dim=2)
+    vals = torch.cat([t64(vc[:, :, :p0]), v], dim=2)
+    mask = torch.arange(p0 + t)[None, :] <= pos.long()[:, None]
+    o = F.scaled_dot_product_attention(rope(q), keys, vals, attn_mask=mask, enable_gqa=True)
+    X1 = X + F.linear(o.transpose(1, 2).reshape(1, t, hq * d), t64(w["o_proj"]))
+    H2 = F.rms_norm(X1, (hs,), t64(w["post_attention_layernorm"]), eps)
+    ref = X1 + F.linear(F.silu(F.linear(H2, t64(w["gate_proj"]))) * F.linear(H2, t64(w["up_proj"])),
+                        t64(w["down_proj"]))
+    assert np.abs(y - ref.numpy()).max() < 1e-11
+
+
 def test_stack_applies_final_norm_after_last_layer():
     cfg = tiny_cfg()
     ws = [si.layer_weights(cfg, layer=l, seed=17) for l in range(3)]

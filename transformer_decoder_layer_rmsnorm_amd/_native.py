@@ -25,7 +25,7 @@ QWEN3_BF16 = 1
 
 EXPORTED = (
     "qwen3_layer_create", "qwen3_layer_destroy", "qwen3_layer_workspace_size",
-    "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_decode",
+    "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_prefill_at", "qwen3_layer_decode",
     "qwen3_rmsnorm", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
     "qwen3_status_string", "qwen3_last_error",
 )
@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         "qwen3_layer_workspace_size": ([P, I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "qwen3_layer_workspace_layout": ([P, I32, I32, I32, ctypes.POINTER(WorkspaceLayout)], ctypes.c_int),
         "qwen3_layer_prefill": ([P, P, P, I32, I32, P, P, I32, P, SZ, P], ctypes.c_int),
+        "qwen3_layer_prefill_at": ([P, P, P, I32, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_layer_decode": ([P, P, P, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_rmsnorm": ([P, P, P, I64, I32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_layer_set_profiling": ([P, I32], ctypes.c_int),
@@ -159,11 +160,20 @@ class Layer:
               "qwen3_layer_workspace_layout")
         return out
 
-    def prefill(self, x, y, k_cache, v_cache, workspace, stream=None) -> None:
+    def prefill(self, x, y, k_cache, v_cache, workspace, stream=None, start_positions=None) -> None:
+        """Prefill; with start_positions (one int per sequence) the tokens continue a cache that
+        already holds that many keys and values (qwen3_layer_prefill_at)."""
         b, t = x.shape[0], x.shape[1]
-        check(lib().qwen3_layer_prefill(self._h, _ptr(x), _ptr(y), b, t, _ptr(k_cache), _ptr(v_cache),
-                                        k_cache.shape[2], _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                        _stream(stream)), "qwen3_layer_prefill")
+        nbytes = workspace.numel() * workspace.element_size()
+        if start_positions is None:
+            check(lib().qwen3_layer_prefill(self._h, _ptr(x), _ptr(y), b, t, _ptr(k_cache), _ptr(v_cache),
+                                            k_cache.shape[2], _ptr(workspace), nbytes, _stream(stream)),
+                  "qwen3_layer_prefill")
+        else:
+            starts = (ctypes.c_int32 * b)(*[int(v) for v in start_positions])
+            check(lib().qwen3_layer_prefill_at(self._h, _ptr(x), _ptr(y), b, t, starts, _ptr(k_cache),
+                                               _ptr(v_cache), k_cache.shape[2], _ptr(workspace), nbytes,
+                                               _stream(stream)), "qwen3_layer_prefill_at")
 
     def decode(self, x, y, cache_lens, k_cache, v_cache, workspace, stream=None) -> None:
         b = x.shape[0]

@@ -347,7 +347,8 @@ qwen3_status qwen3_layer_workspace_size(const qwen3_layer* L, int32_t batch, int
     if (!bytes) return fail(QWEN3_ERR_INVALID_ARGUMENT, "bytes is NULL");
     qwen3_status st = check_sizes(L, batch, seq_len, cap);
     if (st != QWEN3_OK) return st;
-    *bytes = std::max(make_layout(L->cfg, batch, seq_len, 0).prefill_end, make_layout(L->cfg, batch, 1, cap).total);
+    // prefill (with room for device-side start positions) or decode over `cap` slots
+    *bytes = std::max(make_layout(L->cfg, batch, seq_len, 0).total, make_layout(L->cfg, batch, 1, cap).total);
     return QWEN3_OK;
 }
 
@@ -373,27 +374,52 @@ qwen3_status qwen3_layer_workspace_layout(const qwen3_layer* L, int32_t batch, i
     return QWEN3_OK;
 }
 
-qwen3_status qwen3_layer_prefill(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
-                                 void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+qwen3_status qwen3_layer_prefill_at(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                    const int32_t* start_positions, void* k_cache, void* v_cache,
+                                    int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream) {
     qwen3_status st = check_sizes(L, batch, seq_len, cache_capacity);
     if (st != QWEN3_OK) return st;
     if (!x || !y || !k_cache || !v_cache || !workspace)
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, y, k_cache, v_cache and workspace must be non-NULL");
     if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
-    if (seq_len > cache_capacity)
-        return fail(QWEN3_ERR_OUT_OF_RANGE, "seq_len %d exceeds cache_capacity %d", seq_len, cache_capacity);
-    if (seq_len > L->cfg.max_position_embeddings)
-        return fail(QWEN3_ERR_OUT_OF_RANGE, "seq_len %d exceeds max_position_embeddings %d", seq_len,
-                    L->cfg.max_position_embeddings);
+    bool any_start = false;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t p0 = start_positions ? start_positions[b] : 0;
+        if (p0 < 0) return fail(QWEN3_ERR_OUT_OF_RANGE, "start_positions[%d] = %lld is negative", b, (long long)p0);
+        if (p0 + seq_len > cache_capacity)
+            return fail(QWEN3_ERR_OUT_OF_RANGE, "sequence %d: start %lld + seq_len %d exceeds cache_capacity %d", b,
+                        (long long)p0, seq_len, cache_capacity);
+        if (p0 + seq_len > L->cfg.max_position_embeddings)
+            return fail(QWEN3_ERR_OUT_OF_RANGE, "sequence %d: start %lld + seq_len %d exceeds max_position_embeddings %d",
+                        b, (long long)p0, seq_len, L->cfg.max_position_embeddings);
+        any_start |= p0 != 0;
+    }
     const Layout lay = make_layout(L->cfg, batch, seq_len, 0);
-    if (workspace_bytes < lay.prefill_end)
-        return fail(QWEN3_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, prefill needs %zu", workspace_bytes,
-                    lay.prefill_end);
+    const bool via_workspace = any_start && batch > kInlinePositions;
+    const size_t need = via_workspace ? lay.total : lay.prefill_end;
+    if (workspace_bytes < need)
+        return fail(QWEN3_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, prefill needs %zu", workspace_bytes, need);
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
     SeqPositions pos{};
-    return run_layer(L, x, y, batch, seq_len, k_cache, v_cache, cache_capacity, static_cast<char*>(workspace), lay,
-                     pos, false, static_cast<hipStream_t>(stream));
+    if (any_start && !via_workspace) {
+        pos.n_inline = batch;
+        for (int b = 0; b < batch; ++b) pos.inl[b] = start_positions[b];
+    } else if (via_workspace) {
+        const hipError_t e = hipMemcpyAsync(ws + lay.lens, start_positions, sizeof(int32_t) * batch,
+                                            hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying start_positions: %s", hipGetErrorString(e));
+        pos.dev = reinterpret_cast<const int32_t*>(ws + lay.lens);
+    }
+    return run_layer(L, x, y, batch, seq_len, k_cache, v_cache, cache_capacity, ws, lay, pos, false, s);
+}
+
+qwen3_status qwen3_layer_prefill(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                 void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return qwen3_layer_prefill_at(L, x, y, batch, seq_len, nullptr, k_cache, v_cache, cache_capacity, workspace,
+                                  workspace_bytes, stream);
 }
 
 qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
