@@ -86,12 +86,14 @@ typedef struct qwen3_layer qwen3_layer;
  *   x1    [M, H]            residual after attention (always fp32)
  *   h2    [M, H]            post-attention RMSNorm output (dtype)
  *   act   [M, I]            silu(gate) * up (dtype)
- *   lens  [B]               int32 copy of decode cache lengths
+ *   part_gemm [P, M, H]     fp32 split-K partial sums of o_proj (bf16 prefill when too
+ *                           few output tiles fill the GPU; P = 0 otherwise)
+ *   lens  [B]               int32 copy of decode cache lengths / prefill start positions
  *   part_o  [B, Hq, S, D]   fp32 split-KV partial outputs (decode)
  *   part_ml [B, Hq, S, 2]   fp32 split-KV running max (log2 units) and sum
  * where S = number of key splits for cache_capacity keys. */
 typedef struct {
-    size_t h, qkv, qhat, attn, x1, h2, act, lens, part_o, part_ml;
+    size_t h, qkv, qhat, attn, x1, h2, act, part_gemm, lens, part_o, part_ml;
     size_t total;
     int32_t decode_splits;   /* S */
     int32_t split_keys;      /* keys per split */

@@ -51,7 +51,7 @@ class Weights(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("h", "qkv", "qhat", "attn", "x1", "h2", "act", "lens", "part_o", "part_ml", "total")] + \
+                ("h", "qkv", "qhat", "attn", "x1", "h2", "act", "part_gemm", "lens", "part_o", "part_ml", "total")] + \
                [("decode_splits", ctypes.c_int32), ("split_keys", ctypes.c_int32)]
 
 

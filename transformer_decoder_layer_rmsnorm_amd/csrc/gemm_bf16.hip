@@ -45,6 +45,7 @@ struct DevGemm {
     const void* resid;
     int M, N, K;
     int tiles_m, tiles_n;
+    int splits;           // PartialF32: number of K ranges (one fp32 slab [M, N] each)
 };
 
 __device__ __forceinline__ const bf16* seg_row(const DevGemm& p, int n) {
@@ -64,6 +65,8 @@ __device__ __forceinline__ void epilogue_store(const DevGemm& p, int row, int co
     } else if constexpr (EPI == Epilogue::ResidF32In) {
         const float r = static_cast<const float*>(p.resid)[(int64_t)row * p.N + col];
         static_cast<bf16*>(p.out)[(int64_t)row * p.N + col] = (bf16)(r + v);
+    } else if constexpr (EPI == Epilogue::PartialF32) {
+        static_cast<float*>(p.out)[(int64_t)row * p.N + col] = v;   // p.out already at this split's slab
     }
 }
 
@@ -125,9 +128,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
+    // split-K: workgroup blockIdx.x covers tile blockIdx.x % tiles over K range blockIdx.x / tiles
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int split = (int)blockIdx.x / tiles;
     int tm, tn;
-    tile_of(p, blockIdx.x, tm, tn);
+    tile_of(p, (int)blockIdx.x - split * tiles, tm, tn);
     const int m0 = tm * BM;
+    const int nk = p.K / BK / p.splits;
+    const int k_base = split * nk * BK;
 
     // ---- global -> register loaders (chunk c = tid + NT j: row c / 8, 16-byte chunk c % 8)
     const bf16* ga[CA];
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
         const int c = tid + NT * j;
         const int row = c >> 3, ch = c & 7;
         la[j] = row * LP + ch * 8;
-        ga[j] = p.a + (int64_t)min(m0 + row, p.M - 1) * p.K + ch * 8;
+        ga[j] = p.a + (int64_t)min(m0 + row, p.M - 1) * p.K + k_base + ch * 8;
     }
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
@@ -149,9 +157,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
             // B tile rows in blocks of 32: gate, up, gate, up, ... of output columns
             // tn*BN/2 + 32*(row/64) + row%32
             const int n = tn * (BN / 2) + (row >> 6) * 32 + (row & 31);
-            gb[j] = p.b[(row >> 5) & 1] + (int64_t)n * p.K + ch * 8;
+            gb[j] = p.b[(row >> 5) & 1] + (int64_t)n * p.K + k_base + ch * 8;
         } else {
-            gb[j] = seg_row(p, tn * BN + row) + ch * 8;
+            gb[j] = seg_row(p, tn * BN + row) + k_base + ch * 8;
         }
     }
     bf16x8 ra[CA], rb[CB];
@@ -179,7 +187,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     // fragment reads: row (wave's first row) + 32 i + lane%32, chunk 2 kk + lane/32
     const int a_rd = (wm * TM + (lane & 31)) * LP + (lane >> 5) * 8;
     const int b_rd = (wn * TN + (lane & 31)) * LP + (lane >> 5) * 8;
-    const int nk = p.K / BK;
     gload(0);
     lstore(0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -209,7 +216,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
         __syncthreads();
     }
 
-    write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
+    DevGemm q = p;
+    if constexpr (EPI == Epilogue::PartialF32) q.out = static_cast<float*>(p.out) + (int64_t)split * p.M * p.N;
+    write_tile<EPI, BN, TM, TN, FM, FN>(q, acc, m0, tn, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------ large tiles, LDS DMA
@@ -454,6 +463,7 @@ DevGemm make_dev(const GemmArgs& g) {
     p.M = g.M;
     p.N = g.N;
     p.K = g.K;
+    p.splits = g.splits > 1 ? g.splits : 1;
     return p;
 }
 
@@ -484,10 +494,11 @@ bool gemm_bf16_supported(int n_rows, int K) { return n_rows % 128 == 0 && K % 12
 template <Epilogue EPI, int BM, int BN, int WM, int WN>
 static hipError_t run_tile(DevGemm p, hipStream_t s) {
     const int bn_out = (EPI == Epilogue::SwiGLU) ? BN / 2 : BN;
-    if (p.N % bn_out || p.K % BK) return hipErrorInvalidValue;
+    if (EPI != Epilogue::PartialF32) p.splits = 1;
+    if (p.splits < 1 || p.N % bn_out || p.K % (BK * p.splits)) return hipErrorInvalidValue;
     p.tiles_m = (p.M + BM - 1) / BM;
     p.tiles_n = p.N / bn_out;
-    gemm_bf16_kernel<EPI, BM, BN, WM, WN><<<(unsigned)(p.tiles_m * p.tiles_n), WM * WN * 64, 0, s>>>(p);
+    gemm_bf16_kernel<EPI, BM, BN, WM, WN><<<(unsigned)(p.tiles_m * p.tiles_n * p.splits), WM * WN * 64, 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -503,6 +514,8 @@ static hipError_t run_dma_tile(DevGemm p, hipStream_t s) {
 
 template <Epilogue EPI>
 static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
+    // split-K partials: 128x128 tiles, one fp32 slab per K range
+    if constexpr (EPI == Epilogue::PartialF32) return run_tile<EPI, 128, 128, 2, 2>(p, s);
     // The largest tile that still gives at least one workgroup per CU (256 CUs).
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
     const int bn256 = DUAL ? 128 : 256, bn128 = DUAL ? 64 : 128;
@@ -524,8 +537,15 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
         case Epilogue::ResidToF32: return run_epi<Epilogue::ResidToF32>(p, s);
         case Epilogue::SwiGLU: return run_epi<Epilogue::SwiGLU>(p, s);
         case Epilogue::ResidF32In: return run_epi<Epilogue::ResidF32In>(p, s);
+        case Epilogue::PartialF32: return run_epi<Epilogue::PartialF32>(p, s);
     }
     return hipErrorInvalidValue;
+}
+
+int gemm_bf16_splits(int M, int N, int K) {
+    if (M <= 64 || N % 128 || K % (2 * BK) || K < 512) return 1;
+    const long tiles128 = (long)((M + 127) / 128) * (N / 128);
+    return tiles128 < 256 ? 2 : 1;
 }
 
 hipError_t launch_gemv_bf16(const GemmArgs& g, hipStream_t s) {
@@ -536,6 +556,7 @@ hipError_t launch_gemv_bf16(const GemmArgs& g, hipStream_t s) {
         case Epilogue::ResidToF32: return launch_gemv_epi<Epilogue::ResidToF32>(p, s);
         case Epilogue::SwiGLU: return launch_gemv_epi<Epilogue::SwiGLU>(p, s);
         case Epilogue::ResidF32In: return launch_gemv_epi<Epilogue::ResidF32In>(p, s);
+        case Epilogue::PartialF32: return hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
 }

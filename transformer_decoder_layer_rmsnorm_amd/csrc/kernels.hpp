@@ -25,6 +25,11 @@ inline int dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------- RMSNorm
 // y[r, :] = g * x[r, :] / sqrt(mean(x[r, :]^2) + eps), fp32 reduction, one rounding.
+// x1 = x + sum_s part[s] (fp32, written), then y = g * x1 / rms(x1): the residual add of a
+// split-K projection fused with the following RMSNorm.  part holds `splits` slabs [rows, width].
+hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, int splits, float* x1,
+                                   const void* g, void* y, DType yt, int64_t rows, int width, float eps,
+                                   hipStream_t stream);
 hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt,
                           int64_t rows, int width, float eps, hipStream_t stream);
 
@@ -34,6 +39,7 @@ enum class Epilogue : int {
     ResidToF32 = 1,    // out(fp32)   = resid(dtype) + C        (o_proj: x1 = x + attn Wo^T)
     SwiGLU = 2,        // out(dtype)  = silu(C_gate) * C_up     (B0 = gate, B1 = up)
     ResidF32In = 3,    // out(dtype)  = resid(fp32) + C         (down: y = x1 + act Wd^T)
+    PartialF32 = 4,    // out(fp32) + split*M*N = C over the split's K range (split-K partials)
 };
 
 struct GemmArgs {
@@ -45,9 +51,13 @@ struct GemmArgs {
     const void* resid;      // [M, N] residual for the two residual epilogues
     int M, N, K;
     Epilogue epi;
+    int splits;             // PartialF32: K is cut into `splits` equal ranges, one fp32 slab each
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& args, hipStream_t stream);   // MFMA, large M
+// Split count for a bf16 projection whose partial sums can be reduced by the next kernel: 2 when
+// the output has too few 128x128 tiles to fill the CUs and K splits evenly, else 1 (no split).
+int gemm_bf16_splits(int M, int N, int K);
 hipError_t launch_gemv_bf16(const GemmArgs& args, hipStream_t stream);   // MFMA, M <= 64
 hipError_t launch_gemm_f32(const GemmArgs& args, hipStream_t stream);    // fp32 FMA, any shape
 bool gemm_bf16_supported(int N_segment_rows, int K);

@@ -104,7 +104,7 @@ qwen3_status validate_config(const qwen3_config* c) {
 }
 
 struct Layout {
-    size_t h, qkv, qhat, attn, x1, h2, act, prefill_end;
+    size_t h, qkv, qhat, attn, x1, h2, act, part_gemm, prefill_end;
     size_t lens, part_o, part_ml, total;
     int splits;
 };
@@ -124,6 +124,13 @@ Layout make_layout(const qwen3_config& c, int64_t B, int64_t T, int64_t cap) {
     L.x1 = take(M * H * 4);
     L.h2 = take(M * H * es);
     L.act = take(M * I * es);
+    // split-K partial slabs of o_proj (bf16 prefill with few output tiles)
+    int64_t splits = 0;
+    if (c.dtype == QWEN3_BF16 && M <= 0x7fffffff) {
+        const int so = gemm_bf16_splits((int)M, (int)H, (int)(Hq * D));
+        splits = so > 1 ? so : 0;
+    }
+    L.part_gemm = take(splits * M * H * 4);
     L.prefill_end = off;
     L.splits = cap > 0 ? (int)((cap + kDecodeSplitKeys - 1) / kDecodeSplitKeys) : 0;
     L.lens = take(B * 4);
@@ -278,10 +285,24 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     } else {
         STAGE("attention", launch_attention_prefill_bf16(aa, s));
     }
-    STAGE("gemm_o_residual", proj(gemm(attn, {L->w.o_proj}, {H}, x1, x, M, H, Hq * D, Epilogue::ResidToF32)));
-    STAGE("rmsnorm_post", launch_rmsnorm(x1, DType::F32, L->w.post_attention_layernorm, h2, t, M, H, eps, s));
+    // o_proj + residual.  With few output tiles the K range is split and the fp32 partial sums are
+    // added to the residual inside the post-attention RMSNorm (which reads x1 anyway).
+    float* part = reinterpret_cast<float*>(ws + lay.part_gemm);
+    const int so = bf ? gemm_bf16_splits(M, H, Hq * D) : 1;
+    if (so > 1) {
+        GemmArgs go = gemm(attn, {L->w.o_proj}, {H}, part, nullptr, M, H, Hq * D, Epilogue::PartialF32);
+        go.splits = so;
+        STAGE("gemm_o_residual", launch_gemm_bf16(go, s));
+        STAGE("rmsnorm_post", launch_residual_rmsnorm(x, t, part, so, static_cast<float*>(x1),
+                                                      L->w.post_attention_layernorm, h2, t, M, H, eps, s));
+    } else {
+        STAGE("gemm_o_residual", proj(gemm(attn, {L->w.o_proj}, {H}, x1, x, M, H, Hq * D, Epilogue::ResidToF32)));
+        STAGE("rmsnorm_post", launch_rmsnorm(x1, DType::F32, L->w.post_attention_layernorm, h2, t, M, H, eps, s));
+    }
     STAGE("gemm_gate_up_swiglu", proj(gemm(h2, {L->w.gate_proj, L->w.up_proj}, {I, I}, act, nullptr, M, I, H,
                                            Epilogue::SwiGLU)));
+    // down_proj + residual in the GEMM epilogue (a split here would need a separate reduction pass,
+    // which costs what the split saves)
     STAGE("gemm_down_residual", proj(gemm(act, {L->w.down_proj}, {H}, y, x1, M, H, I, Epilogue::ResidF32In)));
 #undef STAGE
     return QWEN3_OK;
@@ -365,6 +386,7 @@ qwen3_status qwen3_layer_workspace_layout(const qwen3_layer* L, int32_t batch, i
     out->x1 = lay.x1;
     out->h2 = lay.h2;
     out->act = lay.act;
+    out->part_gemm = lay.part_gemm;
     out->lens = lay.lens;
     out->part_o = lay.part_o;
     out->part_ml = lay.part_ml;

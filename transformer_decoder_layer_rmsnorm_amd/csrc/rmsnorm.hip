@@ -7,6 +7,11 @@
 //
 // Memory-bound: each row is read once (16-byte loads, kept in registers up to 4096 wide) and
 // written once.  Four rows per 256-thread workgroup.
+//
+// Split-K residual form: when o_proj's K range is split across workgroups, its fp32 partial
+// slabs are summed here, in a fixed order (deterministic), together with the residual:
+// x1 = x + sum_s part_s, written in fp32, then normalised ("17. A modern architecture: Qwen3",
+// section The whole model, Qwen3Layer: x1 = x + attn(...), then post_attention_layernorm(x1)).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -72,6 +77,69 @@ static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t ro
     const dim3 grid((unsigned)((rows + 3) / 4));
     rmsnorm_kernel<TX, TY, 8><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
                                                    static_cast<TY*>(y), rows, width, eps);
+    return hipGetLastError();
+}
+
+
+template <typename TX, typename TY>
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restrict__ x, const float* __restrict__ part,
+                                                               int splits, float* __restrict__ x1,
+                                                               const TY* __restrict__ g, TY* __restrict__ y,
+                                                               int64_t rows, int width, float eps) {
+    constexpr int MAXC = 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int64_t off = row * width;
+    const int64_t slab = rows * width;
+    const int nchunk = width >> 3;
+    float v[MAXC][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+        const int c = lane + j * kWave;
+        if (c < nchunk) {
+            load8(x + off + c * 8, v[j]);
+            for (int sp = 0; sp < splits; ++sp) {
+                float pv[8];
+                load8(part + sp * slab + off + c * 8, pv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[j][i] += pv[i];
+            }
+            store8(x1 + off + c * 8, v[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+        }
+    }
+    const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+        const int c = lane + j * kWave;
+        if (c < nchunk) {
+            float gv[8], o[8];
+            load8(g + c * 8, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = gv[i] * (v[j][i] * rstd);
+            store8(y + off + c * 8, o);
+        }
+    }
+}
+
+hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, int splits, float* x1, const void* g,
+                                   void* y, DType yt, int64_t rows, int width, float eps, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if ((width & 7) || width > 8 * 8 * kWave || splits < 1) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (xt == DType::BF16 && yt == DType::BF16)
+        residual_rmsnorm_kernel<bf16, bf16><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), part, splits, x1,
+                                                                  static_cast<const bf16*>(g), static_cast<bf16*>(y),
+                                                                  rows, width, eps);
+    else if (xt == DType::F32 && yt == DType::F32)
+        residual_rmsnorm_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), part, splits, x1,
+                                                                    static_cast<const float*>(g), static_cast<float*>(y),
+                                                                    rows, width, eps);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
