@@ -51,6 +51,22 @@ def test_qwen3_8b_layer_prefill_sampled_rows():
     assert_bf16_parity(got, ref, f"y at {len(ts)} sampled rows")
 
 
+def test_qwen3_8b_layer_prefill_ragged_tail_rows():
+    """8B shapes at T = 2600 (10 whole 256-row tiles plus a 40-row tail): the QKV and gate/up
+    projections take the long-K ping-pong GEMM with a partial last row tile, o_proj and down
+    the smaller tiles; rows in and around the tail are checked."""
+    wl = si.WORKLOADS["qwen3-8b-layer-prefill"]
+    cfg = wl.cfg
+    t_len = 2600
+    log(f"8B-shaped layer: B1 T{t_len}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed)
+    x = si.layer_input(cfg, 1, t_len, seed=wl.seed)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    ts = [0, 255, 256, 1999, 2559, 2560, 2561, 2580, 2598, 2599]
+    ref = oracle.layer_prefill_rows(x, gl.w_np, cfg, [(0, t) for t in ts])
+    assert_bf16_parity(to_np(y)[0, ts], ref, f"y at {len(ts)} rows incl. the 40-row tail")
+
+
 def test_qwen3_8b_decode_32k_every_row():
     wl = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
     cfg = wl.cfg

@@ -11,7 +11,10 @@
 // wave's LDS base + 16 l, without passing through VGPRs), BK = 32 per stage and four stages in
 // flight, so a k-slab is requested three stages before it is used.  LDS rows are unpadded 64-byte
 // rows whose four 16-byte chunks are XOR-swizzled by row, which keeps fragment reads free of bank
-// conflicts; each load instruction covers 16 rows of one operand.
+// conflicts; each load instruction covers 16 rows of one operand.  For long K (>= 2048) a
+// ping-pong variant of the same tile is used instead: 64-k stages with 128-byte LDS rows (every
+// load moves whole cache lines) and the two wave groups of each SIMD alternating between memory
+// and matrix phases (see gemm_bf16_pp_kernel).
 //
 // Smaller tiles (128 x 128 on 4 waves; 64 x 64, or 64 x 128 for SwiGLU, when fewer than 256
 // tiles would remain) keep a register prefetch: BK = 64, two LDS stages, the next k-slab fetched
@@ -372,6 +375,178 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dma_kernel(DevGemm p) 
     write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
 }
 
+
+// ------------------------------------------------------------------ large tiles, long K: ping-pong
+// 256 x 256 tiles on 8 waves (4 x 2, each wave 64 x 128), BK = 64 per stage in two LDS stages of
+// 128-byte rows (8 chunks of 16 bytes, XOR-swizzled by (row >> 1) & 7), so that every DMA
+// instruction moves 8 rows x 128 contiguous bytes: whole cache lines, which measurably lowers the
+// traffic and power of the operand stream compared with 64-byte row segments.
+//
+// Waves 0-3 and 4-7 (one of each per SIMD) alternate, offset by one phase through an extra
+// barrier: while one group issues its LDS fragment reads and DMA requests, the other runs 16
+// MFMAs, so each SIMD's matrix core is fed by one wave at a time without either waiting on LDS.
+// A phase covers one 32-row half i of the wave's A rows over the whole 64-k stage; the B
+// fragments of the stage are read in phase 0 and held in registers for phase 1.  So B and the
+// i = 0 rows of A are free one phase early and are refilled two stages ahead (requested in phase
+// (t, 1) for stage t + 2); the i = 1 rows of A are requested in phase (t, 0) for stage t + 1.
+// Every request is waited for four phases after it was issued.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+template <int N> __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+__device__ __forceinline__ void lgkm_wait0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+// at most n loads of this wave in flight; n is one of the counts the schedule below produces
+__device__ __forceinline__ void vm_wait_at_most(int n) {
+    if (n >= 8) vm_wait<8>();
+    else if (n >= 6) vm_wait<6>();
+    else if (n >= 2) vm_wait<2>();
+    else vm_wait<0>();
+}
+
+template <Epilogue EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_pp_kernel(DevGemm p) {
+    constexpr int BM = 256, BN = 256, WN = 2, PK = 64;
+    constexpr int TM = 64, TN = 128, FM = 2, FN = 4;
+    constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
+    constexpr int A_ST = BM * PK, B_ST = BN * PK;
+    __shared__ __attribute__((aligned(1024))) bf16 sA[2 * A_ST];
+    __shared__ __attribute__((aligned(1024))) bf16 sB[2 * B_ST];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int grp = wave >> 2;
+    int tm, tn;
+    tile_of(p, blockIdx.x, tm, tn);
+    const int m0 = tm * BM;
+    const int rowbytes = p.K * 2;
+
+    // DMA instructions of this wave, 8 tile rows each.  A: two per half h (h = 0: rows
+    // 64 w + 0..31 of every wave row w, h = 1: rows 64 w + 32..63); B: four.  A rows past M read
+    // as zeros (the descriptor covers only the valid rows).
+    int4v ra[2][2], rb[4];
+    int ra_row[2][2], rb_row[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = wave * 2 + i;
+            const int tr = (q >> 2) * 64 + 32 * h + (q & 3) * 8;
+            ra_row[h][i] = tr;
+            const int r0 = m0 + tr;
+            const int nrows = max(0, min(8, p.M - r0));
+            ra[h][i] = sgpr_desc(p.a + (int64_t)min(r0, p.M - 1) * p.K, nrows * rowbytes);
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int lr = (wave * 4 + i) * 8;
+        rb_row[i] = lr;
+        const bf16* base;
+        if constexpr (DUAL) {
+            // B tile rows in blocks of 32: gate, up, gate, up, ... of output columns
+            // tn*BN/2 + 32*(row/64) + row%32
+            const int n = tn * (BN / 2) + (lr >> 6) * 32 + (lr & 31);
+            base = p.b[(lr >> 5) & 1] + (int64_t)n * p.K;
+        } else {
+            base = seg_row(p, tn * BN + lr);   // 8 rows never straddle a segment
+        }
+        rb[i] = sgpr_desc(base, 8 * rowbytes);
+    }
+    // lane l moves row 8g + l/8 of its instruction's rows, into physical chunk l % 8, which holds
+    // logical chunk (l % 8) ^ swz8(row); swz8 depends on the parity of g
+    const int r8 = lane >> 3;
+    const int voff_even = r8 * rowbytes + (((lane & 7) ^ swz8(r8)) << 4);
+    const int voff_odd = r8 * rowbytes + (((lane & 7) ^ swz8(8 + r8)) << 4);
+    const unsigned sA_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sA;
+    const unsigned sB_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sB;
+    auto issue_b_a0 = [&](int st) {   // 6 loads
+        const int slot = st & 1;
+        const int soff = st * (PK * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16(rb[i], ((rb_row[i] >> 3) & 1) ? voff_odd : voff_even, soff,
+                  __builtin_amdgcn_readfirstlane(sB_lds + (slot * B_ST + rb_row[i] * PK) * 2));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dma16(ra[0][i], ((ra_row[0][i] >> 3) & 1) ? voff_odd : voff_even, soff,
+                  __builtin_amdgcn_readfirstlane(sA_lds + (slot * A_ST + ra_row[0][i] * PK) * 2));
+    };
+    auto issue_a1 = [&](int st) {     // 2 loads
+        const int slot = st & 1;
+        const int soff = st * (PK * 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            dma16(ra[1][i], ((ra_row[1][i] >> 3) & 1) ? voff_odd : voff_even, soff,
+                  __builtin_amdgcn_readfirstlane(sA_lds + (slot * A_ST + ra_row[1][i] * PK) * 2));
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // fragment reads for k step q (k 16q .. 16q+15): row (wave base) + 32 i + lane % 32,
+    // logical chunk 2q + lane / 32
+    const int fr = lane & 31;
+    int a_rd[4], b_rd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a_rd[q] = (wm * TM + fr) * PK + (((2 * q + (lane >> 5)) ^ swz8(fr)) << 3);
+        b_rd[q] = (wn * TN + fr) * PK + (((2 * q + (lane >> 5)) ^ swz8(fr)) << 3);
+    }
+    const int nst = p.K / PK;
+
+    // Request order: B,A0(0) A1(0) B,A0(1), then per stage t: A1(t+1) in phase (t,0) and
+    // B,A0(t+2) in phase (t,1).  Before a phase's closing barrier each wave waits for the data
+    // the next phase reads: A1(t) at the end of (t,0), B,A0(t+1) at the end of (t,1).
+    issue_b_a0(0);
+    issue_a1(0);
+    if (nst > 1) issue_b_a0(1);
+    vm_wait_at_most(nst > 1 ? 8 : 2);
+    barrier_only();
+    if (grp == 1) barrier_only();
+    bf16x8 af[4], bfr[4][FN];
+    for (int t = 0; t < nst; ++t) {
+        const bf16* pa = sA + (t & 1) * A_ST;
+        const bf16* pb = sB + (t & 1) * B_ST;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // ---- memory phase
+            __builtin_amdgcn_sched_barrier(0);
+            if (i == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) bfr[q][j] = *reinterpret_cast<const bf16x8*>(pb + b_rd[q] + j * 32 * PK);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) af[q] = *reinterpret_cast<const bf16x8*>(pa + a_rd[q] + i * 32 * PK);
+            if (i == 0) {
+                if (t + 1 < nst) issue_a1(t + 1);
+                vm_wait_at_most(t + 1 < nst ? 8 : 0);
+            } else {
+                if (t + 2 < nst) issue_b_a0(t + 2);
+                vm_wait_at_most((t + 1 < nst ? 2 : 0) + (t + 2 < nst ? 6 : 0));
+            }
+            lgkm_wait0();
+            barrier_only();
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- compute phase
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[q], bfr[q][j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_only();
+        }
+    }
+    if (grp == 0) barrier_only();
+    write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
+}
+
 // ------------------------------------------------------------------ skinny (M <= 64)
 template <Epilogue EPI, int MG, int NW>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
@@ -513,6 +688,16 @@ static hipError_t run_dma_tile(DevGemm p, hipStream_t s) {
 }
 
 template <Epilogue EPI>
+static hipError_t run_pp_tile(DevGemm p, hipStream_t s) {
+    const int bn_out = (EPI == Epilogue::SwiGLU) ? 128 : 256;
+    if (p.N % bn_out || p.K % 64 || (int64_t)p.K * 2 * 8 >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    p.tiles_m = (p.M + 255) / 256;
+    p.tiles_n = p.N / bn_out;
+    gemm_bf16_pp_kernel<EPI><<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <Epilogue EPI>
 static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     // split-K partials: 128x128 tiles, one fp32 slab per K range
     if constexpr (EPI == Epilogue::PartialF32) return run_tile<EPI, 128, 128, 2, 2>(p, s);
@@ -521,6 +706,9 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     const int bn256 = DUAL ? 128 : 256, bn128 = DUAL ? 64 : 128;
     const long tiles256 = (long)((p.M + 255) / 256) * (p.N / bn256);
     const long tiles128 = (long)((p.M + 127) / 128) * (p.N / bn128);
+    // long K: the ping-pong kernel (whole-line DMA, two 64-k stages); short K, where its
+    // two-stage fill and drain weigh more, the four-stage 32-k kernel
+    if (tiles256 >= 256 && p.N % bn256 == 0 && p.K % 64 == 0 && p.K >= 2048) return run_pp_tile<EPI>(p, s);
     if (tiles256 >= 256 && p.N % bn256 == 0) return run_dma_tile<EPI, 256, 256, 4, 2, 4>(p, s);
     if (tiles128 >= 256) return run_tile<EPI, 128, 128, 2, 2>(p, s);
     if constexpr (DUAL)
