@@ -15,7 +15,8 @@ reproduced: the GPU path is judged against the exact result).  Sources:
          Q/K normalization, SwiGLU, The whole model.
   [L6]   "Transformer architectures: from BERT to diffusion, lesson 6"
          (xmarva.github.io), sections 3 Grouped-query attention, 4 Training
-         stability (QK-norm formula), 5 Qwen3 in PyTorch, 8 (prefix caching).
+         stability (QK-norm formula), 5 Qwen3 in PyTorch, 8 (prefix caching;
+         batched generation of left-padded prompts).
   [CHK]  "Understand modern AI from the inside out" (Qwen3 layer checklist page),
          items on pre-norm order, q_norm/k_norm placement, rotate-half, scaling,
          GQA, causality, SwiGLU and the float32 RMSNorm.
@@ -30,6 +31,7 @@ __all__ = [
     "rmsnorm", "rope_inv_freq", "rope_rotate", "silu", "swiglu_mlp",
     "gqa_causal_attention", "qk_norm_rope", "layer_prefill", "layer_prefill_rows",
     "layer_decode", "layer_prefill_cached", "stack_prefill",
+    "padded_positions", "masked_attention", "layer_prefill_padded", "layer_decode_padded",
 ]
 
 
@@ -275,3 +277,108 @@ def stack_prefill(x, layer_weights, final_gain, cfg, round_between=None):
         if round_between is not None:
             h = _f64(round_between(h))
     return rmsnorm(h, final_gain, cfg.rms_norm_eps)
+
+
+# ----------------------------------------------------------------------------- left padding
+
+def padded_positions(real):
+    """[L6 section 8, batched generation]: positions are counted from each row's
+    first real token: position = (number of real tokens up to and including this
+    column) - 1, clamped at 0 (so padding columns before any real token sit at 0).
+    real: [..., S] booleans -> int positions of the same shape."""
+    real = np.asarray(real, dtype=bool)
+    return np.maximum(np.cumsum(real, axis=-1) - 1, 0)
+
+
+def masked_attention(q, k, v, visible):
+    """Scaled softmax attention over an explicit visibility matrix, grouped KV heads
+    as in gqa_causal_attention ([L6 section 3]).  visible: [Tq, Tk] booleans (every
+    row must see at least one key).  q: [Hq, Tq, D]; k, v: [Hkv, Tk, D]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    hq, _, d = q.shape
+    group = hq // k.shape[0]
+    out = np.empty_like(q)
+    for h in range(hq):
+        kv = h // group
+        scores = np.where(visible, (q[h] @ k[kv].T) / np.sqrt(d), -np.inf)
+        scores = scores - scores.max(axis=-1, keepdims=True)
+        weights = np.exp(scores)
+        weights = weights / weights.sum(axis=-1, keepdims=True)
+        out[h] = weights @ v[kv]
+    return out
+
+
+def _padded_real(start, pad, length):
+    """Slots 0..length-1 of one sequence: real except the padding run [start, start+pad)."""
+    slots = np.arange(length)
+    return ~((slots >= start) & (slots < start + pad))
+
+
+def layer_prefill_padded(x, w, cfg, k_cache, v_cache, starts, pads):
+    """Prefill of rows padded on the left, on top of an optional shared prefix.
+
+    [L6 section 8, batched generation]: prompts of different lengths are padded
+    on the left so every row ends in the same column; padding gets no attention;
+    positions count from each row's first real token; every token may see itself,
+    so a row of pure padding never attends to nothing.  The mask is
+    (causal & real_key) | itself.  With a prefix (keys and values of a shared start
+    computed once), the prefix columns are real and come first.
+    Sequence b holds starts[b] cached (rotated) prefix keys in slots 0..starts[b]-1;
+    its T new tokens go to slots starts[b]+t, and the first pads[b] of them are
+    padding.  x: [B, T, H]; k_cache, v_cache: per sequence [Hkv, >= start, D]
+    (or [B, Hkv, cap, D]).  Returns y [B,T,H], khat_new [B,Hkv,T,D], v_new
+    [B,Hkv,T,D] (what goes to slots starts[b]..starts[b]+T-1, padding included)."""
+    hsize, hq, hkv, d = _dims(cfg)
+    x = _f64(x)
+    bsz, t = x.shape[0], x.shape[1]
+    y = np.empty_like(x)
+    khat_new = np.empty((bsz, hkv, t, d))
+    v_new = np.empty((bsz, hkv, t, d))
+    for b in range(bsz):
+        p0, pad = int(starts[b]), int(pads[b])
+        real = _padded_real(p0, pad, p0 + t)                                  # [p0+T] slots
+        pos_all = padded_positions(real).astype(np.float64)
+        pos = pos_all[p0:]
+        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
+        keys = np.concatenate([_f64(k_cache[b])[:, :p0], khat], axis=1)
+        vals = np.concatenate([_f64(v_cache[b])[:, :p0], v], axis=1)
+        qslot = np.arange(p0, p0 + t)[:, None]
+        kslot = np.arange(p0 + t)[None, :]
+        visible = ((kslot <= qslot) & real[None, :]) | (kslot == qslot)
+        attn = masked_attention(qhat, keys, vals, visible)
+        x1 = x[b] + attn.transpose(1, 0, 2).reshape(t, hq * d) @ _f64(w["o_proj"]).T
+        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
+        khat_new[b], v_new[b] = khat, v
+    return y, khat_new, v_new
+
+
+def layer_decode_padded(x, w, cfg, k_cache, v_cache, cache_lens, pad_starts, pad_lens):
+    """One new token per sequence after a padded prefill ([L6 section 8, batched
+    generation]: each step appends a real column, the mask stays the row's real
+    columns, and the position advances by one from the last prompt position).
+    The new token of sequence b goes to slot cache_lens[b], sits at position
+    (real slots before it) = cache_lens[b] - pad_lens[b], and attends the real
+    cached keys (slots outside [pad_starts[b], pad_starts[b] + pad_lens[b])) and
+    itself.  Returns y [B,1,H], khat_new [B,Hkv,D], v_new [B,Hkv,D]."""
+    hsize, hq, hkv, d = _dims(cfg)
+    x = _f64(x)
+    bsz = x.shape[0]
+    y = np.empty_like(x)
+    khat_new = np.empty((bsz, hkv, d))
+    v_new = np.empty((bsz, hkv, d))
+    for b in range(bsz):
+        n = int(cache_lens[b])
+        real = np.append(_padded_real(int(pad_starts[b]), int(pad_lens[b]), n), True)   # [n+1]
+        pos = np.array([float(padded_positions(real)[-1])])
+        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
+        keys = np.concatenate([_f64(k_cache[b])[:, :n], khat], axis=1)
+        vals = np.concatenate([_f64(v_cache[b])[:, :n], v], axis=1)
+        attn = masked_attention(qhat, keys, vals, real[None, :])
+        x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
+        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
+        khat_new[b], v_new[b] = khat[:, 0], v[:, 0]
+    return y, khat_new, v_new

@@ -411,6 +411,102 @@ def test_cached_prefill_matches_library_assembly_on_given_cache():
     assert np.abs(y - ref.numpy()).max() < 1e-11
 
 
+
+# ---------------------------------------------------------------- left padding (lesson 6, section 8)
+
+def test_padded_positions_page_rule():
+    g = golden("left_padding_positions.json")
+    for case in g["cases"]:
+        assert oracle.padded_positions(case["real"]).tolist() == case["positions"]
+
+
+def test_padded_prefill_real_rows_equal_unpadded_prefill():
+    # padding gets no attention and positions count from the first real token: the real rows
+    # of a left-padded row equal the plain prefill of its real tokens, and their keys/values
+    # equal that prefill's cache
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=21)
+    t = 11
+    pads = [0, 4, 10]
+    x = si.layer_input(cfg, 3, t, seed=21)
+    kc = np.zeros((3, 2, t, 32))
+    y, knew, vnew = oracle.layer_prefill_padded(x, w, cfg, kc, kc, [0, 0, 0], pads)
+    for b, pad in enumerate(pads):
+        ref = oracle.layer_prefill(x[b:b + 1, pad:], w, cfg)
+        np.testing.assert_allclose(y[b, pad:], ref["y"][0], atol=1e-12)
+        np.testing.assert_allclose(knew[b, :, pad:], ref["khat"][0], atol=1e-12)
+        np.testing.assert_allclose(vnew[b, :, pad:], ref["v"][0], atol=1e-12)
+
+
+def test_padded_prefill_padding_query_sees_only_itself():
+    # every token sees itself, and a padding token (no real token before it) sees nothing
+    # else: its attention output is its own value vector, so its row is the layer applied to
+    # a one-token sequence at position 0
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=22)
+    x = si.layer_input(cfg, 1, 6, seed=22)
+    kc = np.zeros((1, 2, 6, 32))
+    y, _, _ = oracle.layer_prefill_padded(x, w, cfg, kc, kc, [0], [3])
+    for t in range(3):
+        ref = oracle.layer_prefill(x[:, t:t + 1], w, cfg)["y"][0, 0]
+        np.testing.assert_allclose(y[0, t], ref, atol=1e-12)
+
+
+def test_padded_prefill_with_prefix_equals_cached_prefill():
+    # a shared prefix followed by left-padded rows: the real rows equal a prefill onto the
+    # prefix cache of the real tokens alone (positions continue from the prefix length)
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=23)
+    p0, t = 5, 8
+    prefix = si.layer_input(cfg, 1, p0, seed=23)
+    pre = oracle.layer_prefill(prefix, w, cfg)
+    kc = np.repeat(pre["khat"], 2, axis=0)
+    vc = np.repeat(pre["v"], 2, axis=0)
+    x = si.layer_input(cfg, 2, t, seed=24)
+    pads = [0, 3]
+    y, knew, vnew = oracle.layer_prefill_padded(x, w, cfg, kc, vc, [p0, p0], pads)
+    for b, pad in enumerate(pads):
+        ref_y, ref_k, ref_v = oracle.layer_prefill_cached(x[b:b + 1, pad:], w, cfg, kc[b:b + 1], vc[b:b + 1], [p0])
+        np.testing.assert_allclose(y[b, pad:], ref_y[0], atol=1e-12)
+        np.testing.assert_allclose(knew[b, :, pad:], ref_k[0], atol=1e-12)
+
+
+def test_padded_decode_equals_unpadded_decode():
+    # after a left-padded prefill, a decode step attends the real keys and itself at position
+    # (real tokens so far): equal to decoding the unpadded sequence
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=25)
+    t = 9
+    pads = [2, 0, 6]
+    x = si.layer_input(cfg, 3, t + 1, seed=25)
+    cap = t + 1
+    kc = np.zeros((3, 2, cap, 32))
+    vc = np.zeros((3, 2, cap, 32))
+    _, knew, vnew = oracle.layer_prefill_padded(x[:, :t], w, cfg, kc, vc, [0, 0, 0], pads)
+    kc[:, :, :t], vc[:, :, :t] = knew, vnew
+    y, kd, vd = oracle.layer_decode_padded(x[:, t:], w, cfg, kc, vc, [t] * 3, [0, 0, 0], pads)
+    for b, pad in enumerate(pads):
+        real = t - pad
+        kr = kc[b:b + 1, :, pad:t]
+        vr = vc[b:b + 1, :, pad:t]
+        ref, rk, rv = oracle.layer_decode(x[b:b + 1, t:], w, cfg, kr, vr, [real])
+        np.testing.assert_allclose(y[b], ref[0], atol=1e-12)
+        np.testing.assert_allclose(kd[b], rk[0], atol=1e-12)
+        np.testing.assert_allclose(vd[b], rv[0], atol=1e-12)
+
+
+def test_masked_attention_reduces_to_causal():
+    # with the causal mask and no padding, the explicit-mask attention is the causal one
+    rng = np.random.default_rng(26)
+    q = rng.standard_normal((4, 7, 16))
+    k = rng.standard_normal((2, 7, 16))
+    v = rng.standard_normal((2, 7, 16))
+    pos = np.arange(7)
+    causal = pos[None, :] <= pos[:, None]
+    np.testing.assert_allclose(oracle.masked_attention(q, k, v, causal),
+                               oracle.gqa_causal_attention(q, k, v, pos, pos), atol=1e-13)
+
+
 def test_stack_applies_final_norm_after_last_layer():
     cfg = tiny_cfg()
     ws = [si.layer_weights(cfg, layer=l, seed=17) for l in range(3)]
