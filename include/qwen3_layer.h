@@ -88,7 +88,8 @@ typedef struct qwen3_layer qwen3_layer;
  *   act   [M, I]            silu(gate) * up (dtype)
  *   part_gemm [P, M, H]     fp32 split-K partial sums of o_proj (bf16 prefill when too
  *                           few output tiles fill the GPU; P = 0 otherwise)
- *   lens  [B]               int32 copy of decode cache lengths / prefill start positions
+ *   lens  [3, B]            int32 copies of the first slots (decode cache lengths / prefill
+ *                           start positions), padding starts and padding lengths
  *   part_o  [B, Hq, S, D]   fp32 split-KV partial outputs (decode)
  *   part_ml [B, Hq, S, 2]   fp32 split-KV running max (log2 units) and sum
  * where S = number of key splits for cache_capacity keys. */
@@ -157,6 +158,29 @@ qwen3_status qwen3_layer_prefill_at(qwen3_layer* layer, const void* x, void* y, 
                                     void* v_cache, int32_t cache_capacity, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* Prefill of left-padded rows ("Transformer architectures: from BERT to
+ * diffusion, lesson 6", section 8, batched generation: prompts of different
+ * lengths are padded on the left so that every row ends in the same column;
+ * padding gets no attention; positions are counted from each row's first real
+ * token; every token may attend itself).  As qwen3_layer_prefill_at, plus
+ * pad_lens, a HOST array [batch] (NULL = no padding): the first pad_lens[b]
+ * tokens of sequence b are padding.  Their keys and values are still written to
+ * slots start_positions[b] .. start_positions[b] + pad_lens[b] - 1 (the padding
+ * run), but no other token attends them; a padding token attends the keys before
+ * the run (a shared prefix) and itself.  Positions count real tokens: token t
+ * of sequence b sits at position start_b + t - pad_b when it is real and at
+ * max(start_b - 1, 0) when it is padding; its cache slot is start_b + t either
+ * way.  Later decode steps pass the same run to qwen3_layer_decode_padded.
+ * Up to 64 sequences the per-sequence values travel as launch arguments; for
+ * more they are copied into the workspace's `lens` region.
+ * Errors: as qwen3_layer_prefill_at, plus OUT_OF_RANGE for pad_lens[b] < 0 or
+ * pad_lens[b] > seq_len. */
+qwen3_status qwen3_layer_prefill_padded(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                        int32_t seq_len, const int32_t* start_positions,
+                                        const int32_t* pad_lens, void* k_cache, void* v_cache,
+                                        int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* Decode: one new token per sequence; x, y are [batch, 1, H].  cache_lens is a
  * HOST array [batch]: sequence b already holds cache_lens[b] rotated keys and
  * values in slots 0..cache_lens[b]-1.  The new token is at position
@@ -173,6 +197,22 @@ qwen3_status qwen3_layer_decode(qwen3_layer* layer, const void* x, void* y, int3
                                 const int32_t* cache_lens, void* k_cache, void* v_cache,
                                 int32_t cache_capacity, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* Decode after a left-padded prefill ("lesson 6", section 8: each generated
+ * token is a real column; the padding stays unattended).  As qwen3_layer_decode,
+ * plus two HOST arrays [batch] (both NULL = no padding): sequence b's padding run
+ * occupies slots pad_starts[b] .. pad_starts[b] + pad_lens[b] - 1 of its cache.
+ * The new token is written to slot cache_lens[b], sits at position
+ * cache_lens[b] - pad_lens[b] (the real tokens before it) and attends every
+ * cached key outside the run, and itself.
+ * Errors: as qwen3_layer_decode, plus INVALID_ARGUMENT when exactly one of the
+ * two arrays is NULL and OUT_OF_RANGE when a run is not inside
+ * [0, cache_lens[b]). */
+qwen3_status qwen3_layer_decode_padded(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                       const int32_t* cache_lens, const int32_t* pad_starts,
+                                       const int32_t* pad_lens, void* k_cache, void* v_cache,
+                                       int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /* RMSNorm of `rows` rows of `width` elements ("17. A modern architecture:
  * Qwen3", section RMSNorm): y = weight * x / sqrt(mean(x^2) + eps), reduced in

@@ -66,22 +66,22 @@ class GpuLayer:
         n = self.layer.workspace_size(batch, seq_len, cap)
         return torch.empty(n, dtype=torch.uint8, device="cuda")
 
-    def prefill(self, x_dev, cap=None, caches=None, ws=None, y_dev=None, starts=None):
+    def prefill(self, x_dev, cap=None, caches=None, ws=None, y_dev=None, starts=None, pads=None):
         b, t, _ = x_dev.shape
         cap = cap or t
         kc, vc = caches or self.alloc_cache(b, cap)
         ws = ws if ws is not None else self.workspace(b, t, cap)
         y = y_dev if y_dev is not None else torch.empty_like(x_dev)
-        self.layer.prefill(x_dev, y, kc, vc, ws, start_positions=starts)
+        self.layer.prefill(x_dev, y, kc, vc, ws, start_positions=starts, pad_lens=pads)
         torch.cuda.synchronize()
         return y, kc, vc, ws
 
-    def decode(self, x_dev, lens, kc, vc, ws=None, y_dev=None):
+    def decode(self, x_dev, lens, kc, vc, ws=None, y_dev=None, pad_starts=None, pad_lens=None):
         b = x_dev.shape[0]
         cap = kc.shape[2]
         ws = ws if ws is not None else self.workspace(b, 1, cap)
         y = y_dev if y_dev is not None else torch.empty_like(x_dev)
-        self.layer.decode(x_dev, y, lens, kc, vc, ws)
+        self.layer.decode(x_dev, y, lens, kc, vc, ws, pad_starts=pad_starts, pad_lens=pad_lens)
         torch.cuda.synchronize()
         return y, ws
 

@@ -168,6 +168,45 @@ def test_prefill_at_validation_before_launch(layer):
         == nat.QWEN3_ERR_INVALID_ARGUMENT
 
 
+
+def prefill_padded(layer, pads, starts=None, t=4, cap=16, ws_bytes=1 << 30):
+    b = len(pads)
+    sa = None if starts is None else (ctypes.c_int32 * b)(*starts)
+    pa = (ctypes.c_int32 * b)(*pads)
+    return nat.lib().qwen3_layer_prefill_padded(layer, FAKE, FAKE, b, t, sa, pa, FAKE, FAKE, cap, FAKE, ws_bytes,
+                                                None)
+
+
+def test_prefill_padded_validation_before_launch(layer):
+    assert prefill_padded(layer, [0, -1]) == nat.QWEN3_ERR_OUT_OF_RANGE         # negative padding
+    assert prefill_padded(layer, [5]) == nat.QWEN3_ERR_OUT_OF_RANGE             # more padding than tokens
+    assert prefill_padded(layer, [1], starts=[13]) == nat.QWEN3_ERR_OUT_OF_RANGE   # 13 + 4 > 16
+    assert prefill_padded(layer, [1, 2], ws_bytes=100) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+    # more than 64 padded sequences: the per-sequence values go through the `lens` region
+    lay = nat.WorkspaceLayout()
+    assert nat.lib().qwen3_layer_workspace_layout(layer, 65, 4, 0, ctypes.byref(lay)) == nat.QWEN3_OK
+    assert prefill_padded(layer, [1] * 65, ws_bytes=lay.lens) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+    assert lay.part_o - lay.lens >= 3 * 65 * 4
+
+
+def decode_padded(layer, lens, pad_starts, pad_lens, cap=64, ws_bytes=1 << 30):
+    b = len(lens)
+    la = (ctypes.c_int32 * b)(*lens)
+    sa = None if pad_starts is None else (ctypes.c_int32 * b)(*pad_starts)
+    pa = None if pad_lens is None else (ctypes.c_int32 * b)(*pad_lens)
+    return nat.lib().qwen3_layer_decode_padded(layer, FAKE, FAKE, b, la, sa, pa, FAKE, FAKE, cap, FAKE, ws_bytes,
+                                               None)
+
+
+def test_decode_padded_validation_before_launch(layer):
+    assert decode_padded(layer, [10], [0], None) == nat.QWEN3_ERR_INVALID_ARGUMENT     # one array only
+    assert decode_padded(layer, [10], [4], [7]) == nat.QWEN3_ERR_OUT_OF_RANGE          # run past the cache
+    assert decode_padded(layer, [10], [-1], [2]) == nat.QWEN3_ERR_OUT_OF_RANGE
+    assert decode_padded(layer, [10], [0], [-2]) == nat.QWEN3_ERR_OUT_OF_RANGE
+    assert decode_padded(layer, [10, 64], [0, 0], [1, 1]) == nat.QWEN3_ERR_OUT_OF_RANGE   # no free slot
+    assert decode_padded(layer, [10], [0], [3], ws_bytes=100) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_rmsnorm_validation_and_status_strings():
     L = nat.lib()
     assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 4, 12, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_UNSUPPORTED

@@ -25,7 +25,8 @@ QWEN3_BF16 = 1
 
 EXPORTED = (
     "qwen3_layer_create", "qwen3_layer_destroy", "qwen3_layer_workspace_size",
-    "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_prefill_at", "qwen3_layer_decode",
+    "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_prefill_at",
+    "qwen3_layer_prefill_padded", "qwen3_layer_decode", "qwen3_layer_decode_padded",
     "qwen3_rmsnorm", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
     "qwen3_status_string", "qwen3_last_error",
 )
@@ -85,7 +86,11 @@ def lib() -> ctypes.CDLL:
         "qwen3_layer_workspace_layout": ([P, I32, I32, I32, ctypes.POINTER(WorkspaceLayout)], ctypes.c_int),
         "qwen3_layer_prefill": ([P, P, P, I32, I32, P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_layer_prefill_at": ([P, P, P, I32, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
+        "qwen3_layer_prefill_padded": ([P, P, P, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, I32, P,
+                                        SZ, P], ctypes.c_int),
         "qwen3_layer_decode": ([P, P, P, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
+        "qwen3_layer_decode_padded": ([P, P, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                       P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_rmsnorm": ([P, P, P, I64, I32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_layer_set_profiling": ([P, I32], ctypes.c_int),
         "qwen3_layer_read_profile": ([P, ctypes.POINTER(StageTime), I32, ctypes.POINTER(I32)], ctypes.c_int),
@@ -160,12 +165,19 @@ class Layer:
               "qwen3_layer_workspace_layout")
         return out
 
-    def prefill(self, x, y, k_cache, v_cache, workspace, stream=None, start_positions=None) -> None:
+    def prefill(self, x, y, k_cache, v_cache, workspace, stream=None, start_positions=None, pad_lens=None) -> None:
         """Prefill; with start_positions (one int per sequence) the tokens continue a cache that
-        already holds that many keys and values (qwen3_layer_prefill_at)."""
+        already holds that many keys and values (qwen3_layer_prefill_at); with pad_lens the first
+        pad_lens[b] tokens of sequence b are left padding (qwen3_layer_prefill_padded)."""
         b, t = x.shape[0], x.shape[1]
         nbytes = workspace.numel() * workspace.element_size()
-        if start_positions is None:
+        if pad_lens is not None:
+            starts = None if start_positions is None else (ctypes.c_int32 * b)(*[int(v) for v in start_positions])
+            pads = (ctypes.c_int32 * b)(*[int(v) for v in pad_lens])
+            check(lib().qwen3_layer_prefill_padded(self._h, _ptr(x), _ptr(y), b, t, starts, pads, _ptr(k_cache),
+                                                   _ptr(v_cache), k_cache.shape[2], _ptr(workspace), nbytes,
+                                                   _stream(stream)), "qwen3_layer_prefill_padded")
+        elif start_positions is None:
             check(lib().qwen3_layer_prefill(self._h, _ptr(x), _ptr(y), b, t, _ptr(k_cache), _ptr(v_cache),
                                             k_cache.shape[2], _ptr(workspace), nbytes, _stream(stream)),
                   "qwen3_layer_prefill")
@@ -175,12 +187,23 @@ class Layer:
                                                _ptr(v_cache), k_cache.shape[2], _ptr(workspace), nbytes,
                                                _stream(stream)), "qwen3_layer_prefill_at")
 
-    def decode(self, x, y, cache_lens, k_cache, v_cache, workspace, stream=None) -> None:
+    def decode(self, x, y, cache_lens, k_cache, v_cache, workspace, stream=None, pad_starts=None,
+               pad_lens=None) -> None:
+        """One token per sequence; with pad_starts / pad_lens, the cache slots
+        [pad_starts[b], pad_starts[b] + pad_lens[b]) are left padding (qwen3_layer_decode_padded)."""
         b = x.shape[0]
         lens = (ctypes.c_int32 * b)(*[int(v) for v in cache_lens])
+        nbytes = workspace.numel() * workspace.element_size()
+        if pad_lens is not None or pad_starts is not None:
+            starts = None if pad_starts is None else (ctypes.c_int32 * b)(*[int(v) for v in pad_starts])
+            pads = None if pad_lens is None else (ctypes.c_int32 * b)(*[int(v) for v in pad_lens])
+            check(lib().qwen3_layer_decode_padded(self._h, _ptr(x), _ptr(y), b, lens, starts, pads, _ptr(k_cache),
+                                                  _ptr(v_cache), k_cache.shape[2], _ptr(workspace), nbytes,
+                                                  _stream(stream)), "qwen3_layer_decode_padded")
+            return
         check(lib().qwen3_layer_decode(self._h, _ptr(x), _ptr(y), b, lens, _ptr(k_cache), _ptr(v_cache),
-                                       k_cache.shape[2], _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                       _stream(stream)), "qwen3_layer_decode")
+                                       k_cache.shape[2], _ptr(workspace), nbytes, _stream(stream)),
+              "qwen3_layer_decode")
 
     def set_profiling(self, enabled: bool) -> None:
         check(lib().qwen3_layer_set_profiling(self._h, 1 if enabled else 0), "qwen3_layer_set_profiling")

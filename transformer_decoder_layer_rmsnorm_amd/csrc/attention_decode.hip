@@ -81,6 +81,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
     const int kv_len = seq_pos(a.pos, b) + 1;
     const int key0 = split * SK;
     if (key0 >= kv_len) return;
+    int pad_lo, pad_hi;   // left-padding slots of this sequence: never attended by the new token
+    seq_pad(a.pos, b, pad_lo, pad_hi);
     const int nk = min(SK, kv_len - key0);
     const int dc = lane & 15, ks = lane >> 4;
 
@@ -111,7 +113,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
         }
         int head;
         const float sum = key_reduce<G>(s, lane, head);
-        if ((dc & ((16 / G) - 1)) == 0) sP[kk * G + head] = kk < nk ? sum : -INFINITY;
+        const bool visible = (kk < nk) & ((key0 + kk < pad_lo) | (key0 + kk >= pad_hi));
+        if ((dc & ((16 / G) - 1)) == 0) sP[kk * G + head] = visible ? sum : -INFINITY;
     }
     // the first value rows are requested now, so HBM stays busy through the softmax phase
     constexpr int VPRE = 4;

@@ -1,10 +1,11 @@
 // fp32 causal grouped-query attention, any even head_dim <= 128, prefill or decode.
 //
 // Same definition as the bf16 kernels ("lesson 6", section 3: query head h reads KV head
-// floor(h / g); scores scaled by D^-1/2; key visible iff its position <= the query's), for the
-// fp32 storage configuration.  One wavefront per (sequence, head, query): lane l holds
-// features l and l + 64, each key costs one wave reduction, and the softmax is accumulated
-// online in fp32 with exact expf.  Meant for small problems; no tiling.
+// floor(h / g); scores scaled by D^-1/2; key visible iff its slot <= the query's and it is not
+// left padding, or it is the query's own token), for the fp32 storage configuration.  One
+// wavefront per (sequence, head, query): lane l holds features l and l + 64, each key costs one
+// wave reduction, and the softmax is accumulated online in fp32 with exact expf.  Meant for
+// small problems; no tiling.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,7 +23,9 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
     const int b = (int)(gw / ((int64_t)a.T * a.Hq));
     const int kvh = h / (a.Hq / a.Hkv);
     const int D = a.D;
-    const int pos = seq_pos(a.pos, b) + t;
+    const int pos = seq_pos(a.pos, b) + t;   // the query's cache slot
+    int pad_lo, pad_hi;                       // left-padding slots, seen only by themselves
+    seq_pad(a.pos, b, pad_lo, pad_hi);
 
     const float* q = static_cast<const float*>(a.qhat) + (((int64_t)b * a.Hq + h) * a.T + t) * D;
     const float* kb = static_cast<const float*>(a.k_cache) + ((int64_t)b * a.Hkv + kvh) * a.cap * D;
@@ -32,6 +35,7 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
 
     float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
     for (int j = 0; j <= pos; ++j) {
+        if (j >= pad_lo && j < pad_hi && j != pos) continue;
         const float* kr = kb + (int64_t)j * D;
         const float* vr = vb + (int64_t)j * D;
         const float s = wave_sum((in0 ? q0 * kr[lane] : 0.f) + (in1 ? q1 * kr[lane + 64] : 0.f)) * a.scale;

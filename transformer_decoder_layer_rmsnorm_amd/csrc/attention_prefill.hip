@@ -39,6 +39,8 @@
 //    probabilities the PV product actually uses (v_dot2), so the weights sum exactly to one.
 //  * Tiles above the diagonal are never visited; per wave, 32-key blocks that lie entirely
 //    above its queries skip their MFMAs.
+//  * Left-padded batches ("lesson 6", section 8): keys in a sequence's padding slots are masked
+//    for every query but their own token, on the tiles that overlap the padding run.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -64,7 +66,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int HPW, int KS>
+template <int HPW, int KS, bool PAD>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a, float sl2,
                                                                                                    bool pair_tiles) {
     constexpr int WPH = 4 / (HPW * KS);
@@ -112,6 +114,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     const int q0 = (nqt - 1 - qrank) * QB;
     const int qw = q0 + wq * 32;
     const int pos0 = __builtin_amdgcn_readfirstlane(seq_pos(a.pos, b));
+    int pad_lo = 0, pad_hi = 0;   // left-padding slots: attended by nobody but themselves
+    if constexpr (PAD) {
+        seq_pad(a.pos, b, pad_lo, pad_hi);
+        pad_lo = __builtin_amdgcn_readfirstlane(pad_lo);
+        pad_hi = __builtin_amdgcn_readfirstlane(pad_hi);
+    }
     const int kv_len = pos0 + min(q0 + QB, a.T);
     const int ntiles = (kv_len + KT - 1) / KT;
     const int my_pos = pos0 + qw + (lane & 31);
@@ -194,14 +202,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     };
     auto softmax_pv = [&](int t, f32x16 (&sacc)[NKB], const bool (&live)[NKB]) {
         const int k0 = t * KT;
-        if (k0 + KT - 1 > wave_first) {
+        if (k0 + KT - 1 > wave_first || (PAD && k0 < pad_hi && k0 + KT > pad_lo)) {
 #pragma unroll
             for (int i = 0; i < NKB; ++i) {
                 const int kb = (KS == 1) ? i : ph;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    if (key > my_pos) sacc[i][r] = -INFINITY;
+                    // branch-free select (bitwise, not short-circuit operators)
+                    const bool masked =
+                        (key > my_pos) | (PAD & (key >= pad_lo) & (key < pad_hi) & (key != my_pos));
+                    sacc[i][r] = masked ? -INFINITY : sacc[i][r];
                 }
             }
         }
@@ -324,6 +335,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     }
 }
 
+template <bool PAD>
+hipError_t launch_hpw(const AttnArgs& a, int hpw, bool split, dim3 grid, float scale_log2, bool pair_tiles,
+                      hipStream_t stream) {
+    if (hpw == 4)
+        flash_prefill_kernel<4, 1, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+    else if (hpw == 2 && split)
+        flash_prefill_kernel<2, 2, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+    else if (hpw == 2)
+        flash_prefill_kernel<2, 1, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+    else if (split)
+        flash_prefill_kernel<1, 2, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+    else
+        flash_prefill_kernel<1, 1, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -342,17 +369,10 @@ hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) 
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
     const bool pair_tiles = wgs <= 512;   // two workgroups per CU on 256 CUs
-    if (hpw == 4)
-        flash_prefill_kernel<4, 1><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
-    else if (hpw == 2 && split)
-        flash_prefill_kernel<2, 2><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
-    else if (hpw == 2)
-        flash_prefill_kernel<2, 1><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
-    else if (split)
-        flash_prefill_kernel<1, 2><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
-    else
-        flash_prefill_kernel<1, 1><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
-    return hipGetLastError();
+    // the padding-aware variant only when some sequence has left padding
+    const bool pad = a.pos.dev_pad != nullptr || a.pos.n_pad_inline > 0;
+    if (pad) return launch_hpw<true>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
+    return launch_hpw<false>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
 }
 
 }  // namespace q3

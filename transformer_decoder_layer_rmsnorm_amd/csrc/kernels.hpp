@@ -8,17 +8,44 @@ namespace q3 {
 
 enum class DType : int { F32 = 0, BF16 = 1 };
 
-// Position of token 0 of each sequence (== the cache slot it is written to).  Prefill on an
-// empty cache uses all zeros; decode passes the cache lengths, by value for up to
-// kInlinePositions sequences (no host-to-device copy), else through a device array.
+// Per-sequence placement of the tokens of a call.
+//  * first slot: cache slot of token 0 of each sequence (prefill on an empty cache: 0; prefill
+//    onto a cache: its length; decode: the cache length).
+//  * padding: an optional run of cache slots [pad_lo, pad_lo + pad_n) per sequence holding
+//    left-padding tokens ("lesson 6", section 8, batched generation): no other token attends
+//    them (a padding token still attends itself and the real keys before it), and positions
+//    count real tokens only: slot s sits at position s below the run, s - pad_n above it, and
+//    max(pad_lo - 1, 0) inside it (number of real tokens up to it, minus one, clamped at 0).
+// Up to kInlinePositions sequences the values travel by value in the kernel arguments (no
+// host-to-device copy); beyond, through device arrays.
 constexpr int kInlinePositions = 64;
 struct SeqPositions {
-    const int32_t* dev;                 // device array [B], or nullptr
+    const int32_t* dev;                 // device array [B] of first slots, or nullptr
+    const int32_t* dev_pad;             // device array [2B]: pad_lo[B] then pad_n[B], or nullptr
     int32_t n_inline;                   // when dev == nullptr: inl[b] for b < n_inline, else 0
+    int32_t n_pad_inline;               // when dev_pad == nullptr: padding of b < n_pad_inline
     int32_t inl[kInlinePositions];
+    int32_t pad_lo[kInlinePositions];
+    int32_t pad_n[kInlinePositions];
 };
 __device__ __forceinline__ int seq_pos(const SeqPositions& p, int b) {
     return p.dev ? p.dev[b] : (b < p.n_inline ? p.inl[b] : 0);
+}
+// padding run [lo, hi) of sequence b (lo == hi when it has none)
+__device__ __forceinline__ void seq_pad(const SeqPositions& p, int b, int& lo, int& hi) {
+    if (p.dev_pad) {
+        lo = p.dev_pad[b];
+        hi = lo + p.dev_pad[p.n_pad_inline + b];   // n_pad_inline holds B when dev_pad is set
+    } else if (b < p.n_pad_inline) {
+        lo = p.pad_lo[b];
+        hi = lo + p.pad_n[b];
+    } else {
+        lo = hi = 0;
+    }
+}
+// position of cache slot `slot` of a sequence with padding run [lo, hi)
+__device__ __forceinline__ int slot_position(int slot, int lo, int hi) {
+    return slot < lo ? slot : (slot >= hi ? slot - (hi - lo) : max(lo - 1, 0));
 }
 
 inline int dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }

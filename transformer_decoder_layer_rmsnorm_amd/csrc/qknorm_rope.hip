@@ -6,7 +6,8 @@
 // by all heads, applied after the reshape to heads and before RoPE; V is neither normalised
 // nor rotated.  Section Rotary position embeddings: omega_i = theta^(-2i/D), feature i is
 // paired with feature i + D/2 and the pair is turned by p * omega_i; keys enter the cache
-// already rotated.
+// already rotated.  The token's cache slot and its position differ only for left-padded
+// batches ("lesson 6", section 8: positions count a row's real tokens).
 //
 // One 256-thread workgroup per token; the cos/sin of each rotation pair are computed once per
 // token from an angle formed in fp64 (p * omega_i / 2pi, reduced exactly to [-1/2, 1/2] turn,
@@ -32,7 +33,10 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
     const int D = a.D;
     const int half = D >> 1;
     const bool active = lane < half;
-    const int pos = seq_pos(a.pos, b) + t;   // position == cache slot
+    const int slot = seq_pos(a.pos, b) + t;  // cache slot of the token
+    int pad_lo, pad_hi;
+    seq_pad(a.pos, b, pad_lo, pad_hi);
+    const int pos = slot_position(slot, pad_lo, pad_hi);   // RoPE position (real tokens before it)
 
     // cos / sin of p * omega_lane.  The angle is formed in fp64 in turns (p * omega / 2pi),
     // reduced exactly to [-1/2, 1/2] turn, and only then evaluated in fp32 on [-pi, pi].
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
             if (hs >= nheads) break;
             if (hs >= a.Hq + a.Hkv) {  // value head: copied to its cache slot unchanged
                 const int kh = hs - a.Hq - a.Hkv;
-                T* dst = static_cast<T*>(a.v_cache) + (((int64_t)b * a.Hkv + kh) * a.cap + pos) * D;
+                T* dst = static_cast<T*>(a.v_cache) + (((int64_t)b * a.Hkv + kh) * a.cap + slot) * D;
                 if (active) {
                     dst[lane] = from_f32<T>(x0[i]);
                     dst[lane + half] = from_f32<T>(x1[i]);
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
                 dst = static_cast<T*>(a.qhat) + (((int64_t)b * a.Hq + hs) * a.T + t) * D;
             } else {
                 const int kh = hs - a.Hq;
-                dst = static_cast<T*>(a.k_cache) + (((int64_t)b * a.Hkv + kh) * a.cap + pos) * D;
+                dst = static_cast<T*>(a.k_cache) + (((int64_t)b * a.Hkv + kh) * a.cap + slot) * D;
             }
             dst[lane] = from_f32<T>(r0);
             dst[lane + half] = from_f32<T>(r1);
@@ -117,7 +121,10 @@ __global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slot = lane >> 4;          // head slot within a group of four heads
     const int j = lane & 15;             // features 4j..4j+3 and 64+4j..64+4j+3
-    const int pos = seq_pos(a.pos, b) + t;
+    const int cslot = seq_pos(a.pos, b) + t;   // cache slot of the token
+    int pad_lo, pad_hi;
+    seq_pad(a.pos, b, pad_lo, pad_hi);
+    const int pos = slot_position(cslot, pad_lo, pad_hi);
 
     float cs[4], sn[4], gq[8], gk[8];
 #pragma unroll
@@ -145,8 +152,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
     const int ngroups = (nheads + 3) >> 2;
     const bf16* src = static_cast<const bf16*>(a.qkv) + (int64_t)tok * nheads * D + 4 * j;
     bf16* q_dst = static_cast<bf16*>(a.qhat) + ((int64_t)b * a.Hq * a.T + t) * D + 4 * j;
-    bf16* k_dst = static_cast<bf16*>(a.k_cache) + ((int64_t)b * a.Hkv * a.cap + pos) * D + 4 * j;
-    bf16* v_dst = static_cast<bf16*>(a.v_cache) + ((int64_t)b * a.Hkv * a.cap + pos) * D + 4 * j;
+    bf16* k_dst = static_cast<bf16*>(a.k_cache) + ((int64_t)b * a.Hkv * a.cap + cslot) * D + 4 * j;
+    bf16* v_dst = static_cast<bf16*>(a.v_cache) + ((int64_t)b * a.Hkv * a.cap + cslot) * D + 4 * j;
     const int64_t q_stride = (int64_t)a.T * D, kv_stride = (int64_t)a.cap * D;
 
     // the wave's groups are wave, wave + 4, ...; loads for GB of them are issued first

@@ -133,7 +133,7 @@ Layout make_layout(const qwen3_config& c, int64_t B, int64_t T, int64_t cap) {
     L.part_gemm = take(splits * M * H * 4);
     L.prefill_end = off;
     L.splits = cap > 0 ? (int)((cap + kDecodeSplitKeys - 1) / kDecodeSplitKeys) : 0;
-    L.lens = take(B * 4);
+    L.lens = take(B * 4 * 3);   // first slots, padding starts, padding lengths
     L.part_o = take(c.dtype == QWEN3_BF16 ? B * Hq * L.splits * D * 4 : 0);
     L.part_ml = take(c.dtype == QWEN3_BF16 ? B * Hq * L.splits * 2 * 4 : 0);
     L.total = off;
@@ -396,19 +396,24 @@ qwen3_status qwen3_layer_workspace_layout(const qwen3_layer* L, int32_t batch, i
     return QWEN3_OK;
 }
 
-qwen3_status qwen3_layer_prefill_at(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
-                                    const int32_t* start_positions, void* k_cache, void* v_cache,
-                                    int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream) {
+qwen3_status qwen3_layer_prefill_padded(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                        const int32_t* start_positions, const int32_t* pad_lens, void* k_cache,
+                                        void* v_cache, int32_t cache_capacity, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
     qwen3_status st = check_sizes(L, batch, seq_len, cache_capacity);
     if (st != QWEN3_OK) return st;
     if (!x || !y || !k_cache || !v_cache || !workspace)
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, y, k_cache, v_cache and workspace must be non-NULL");
     if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
-    bool any_start = false;
+    bool any_start = false, any_pad = false;
     for (int b = 0; b < batch; ++b) {
         const int64_t p0 = start_positions ? start_positions[b] : 0;
+        const int64_t pad = pad_lens ? pad_lens[b] : 0;
         if (p0 < 0) return fail(QWEN3_ERR_OUT_OF_RANGE, "start_positions[%d] = %lld is negative", b, (long long)p0);
+        if (pad < 0 || pad > seq_len)
+            return fail(QWEN3_ERR_OUT_OF_RANGE, "pad_lens[%d] = %lld is outside [0, seq_len = %d]", b, (long long)pad,
+                        seq_len);
         if (p0 + seq_len > cache_capacity)
             return fail(QWEN3_ERR_OUT_OF_RANGE, "sequence %d: start %lld + seq_len %d exceeds cache_capacity %d", b,
                         (long long)p0, seq_len, cache_capacity);
@@ -416,43 +421,74 @@ qwen3_status qwen3_layer_prefill_at(qwen3_layer* L, const void* x, void* y, int3
             return fail(QWEN3_ERR_OUT_OF_RANGE, "sequence %d: start %lld + seq_len %d exceeds max_position_embeddings %d",
                         b, (long long)p0, seq_len, L->cfg.max_position_embeddings);
         any_start |= p0 != 0;
+        any_pad |= pad != 0;
     }
     const Layout lay = make_layout(L->cfg, batch, seq_len, 0);
-    const bool via_workspace = any_start && batch > kInlinePositions;
+    const bool via_workspace = (any_start || any_pad) && batch > kInlinePositions;
     const size_t need = via_workspace ? lay.total : lay.prefill_end;
     if (workspace_bytes < need)
         return fail(QWEN3_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, prefill needs %zu", workspace_bytes, need);
     char* ws = static_cast<char*>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     SeqPositions pos{};
-    if (any_start && !via_workspace) {
-        pos.n_inline = batch;
-        for (int b = 0; b < batch; ++b) pos.inl[b] = start_positions[b];
-    } else if (via_workspace) {
-        const hipError_t e = hipMemcpyAsync(ws + lay.lens, start_positions, sizeof(int32_t) * batch,
+    if (via_workspace) {
+        std::vector<int32_t> host(3 * (size_t)batch, 0);
+        for (int b = 0; b < batch; ++b) {
+            host[b] = start_positions ? start_positions[b] : 0;
+            host[batch + b] = host[b];
+            host[2 * batch + b] = pad_lens ? pad_lens[b] : 0;
+        }
+        const hipError_t e = hipMemcpyAsync(ws + lay.lens, host.data(), sizeof(int32_t) * host.size(),
                                             hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying start_positions: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying start positions: %s", hipGetErrorString(e));
         pos.dev = reinterpret_cast<const int32_t*>(ws + lay.lens);
+        if (any_pad) {
+            pos.dev_pad = pos.dev + batch;
+            pos.n_pad_inline = batch;
+        }
+    } else {
+        if (any_start) {
+            pos.n_inline = batch;
+            for (int b = 0; b < batch; ++b) pos.inl[b] = start_positions[b];
+        }
+        if (any_pad) {
+            pos.n_pad_inline = batch;
+            for (int b = 0; b < batch; ++b) {
+                pos.pad_lo[b] = start_positions ? start_positions[b] : 0;
+                pos.pad_n[b] = pad_lens[b];
+            }
+        }
     }
     return run_layer(L, x, y, batch, seq_len, k_cache, v_cache, cache_capacity, ws, lay, pos, false, s);
+}
+
+qwen3_status qwen3_layer_prefill_at(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                    const int32_t* start_positions, void* k_cache, void* v_cache,
+                                    int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream) {
+    return qwen3_layer_prefill_padded(L, x, y, batch, seq_len, start_positions, nullptr, k_cache, v_cache,
+                                      cache_capacity, workspace, workspace_bytes, stream);
 }
 
 qwen3_status qwen3_layer_prefill(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
                                  void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    return qwen3_layer_prefill_at(L, x, y, batch, seq_len, nullptr, k_cache, v_cache, cache_capacity, workspace,
-                                  workspace_bytes, stream);
+    return qwen3_layer_prefill_padded(L, x, y, batch, seq_len, nullptr, nullptr, k_cache, v_cache, cache_capacity,
+                                      workspace, workspace_bytes, stream);
 }
 
-qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
-                                void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+qwen3_status qwen3_layer_decode_padded(qwen3_layer* L, const void* x, void* y, int32_t batch,
+                                       const int32_t* cache_lens, const int32_t* pad_starts, const int32_t* pad_lens,
+                                       void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
     qwen3_status st = check_sizes(L, batch, 1, cache_capacity);
     if (st != QWEN3_OK) return st;
     if (!x || !y || !k_cache || !v_cache || !workspace || !cache_lens)
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, y, cache_lens, k_cache, v_cache and workspace must be non-NULL");
+    if ((pad_starts == nullptr) != (pad_lens == nullptr))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "pad_starts and pad_lens must both be given or both be NULL");
     if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace))
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+    bool any_pad = false;
     for (int b = 0; b < batch; ++b) {
         const int n = cache_lens[b];
         if (n < 0 || n >= cache_capacity)
@@ -461,6 +497,13 @@ qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t 
         if (n >= L->cfg.max_position_embeddings)
             return fail(QWEN3_ERR_OUT_OF_RANGE, "position %d of sequence %d reaches max_position_embeddings %d", n, b,
                         L->cfg.max_position_embeddings);
+        if (pad_lens) {
+            const int64_t lo = pad_starts[b], pn = pad_lens[b];
+            if (lo < 0 || pn < 0 || lo + pn > n)
+                return fail(QWEN3_ERR_OUT_OF_RANGE, "sequence %d: padding [%lld, %lld) is not inside its %d cached slots",
+                            b, (long long)lo, (long long)(lo + pn), n);
+            any_pad |= pn != 0;
+        }
     }
     const Layout lay = make_layout(L->cfg, batch, 1, cache_capacity);
     if (workspace_bytes < lay.total)
@@ -472,12 +515,37 @@ qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t 
     if (batch <= kInlinePositions) {
         pos.n_inline = batch;
         for (int b = 0; b < batch; ++b) pos.inl[b] = cache_lens[b];
+        if (any_pad) {
+            pos.n_pad_inline = batch;
+            for (int b = 0; b < batch; ++b) {
+                pos.pad_lo[b] = pad_starts[b];
+                pos.pad_n[b] = pad_lens[b];
+            }
+        }
     } else {
-        const hipError_t e = hipMemcpyAsync(ws + lay.lens, cache_lens, sizeof(int32_t) * batch, hipMemcpyHostToDevice, s);
+        std::vector<int32_t> host(3 * (size_t)batch, 0);
+        for (int b = 0; b < batch; ++b) {
+            host[b] = cache_lens[b];
+            host[batch + b] = any_pad ? pad_starts[b] : 0;
+            host[2 * batch + b] = any_pad ? pad_lens[b] : 0;
+        }
+        const hipError_t e = hipMemcpyAsync(ws + lay.lens, host.data(), sizeof(int32_t) * host.size(),
+                                            hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying cache_lens: %s", hipGetErrorString(e));
         pos.dev = reinterpret_cast<const int32_t*>(ws + lay.lens);
+        if (any_pad) {
+            pos.dev_pad = pos.dev + batch;
+            pos.n_pad_inline = batch;
+        }
     }
     return run_layer(L, x, y, batch, 1, k_cache, v_cache, cache_capacity, ws, lay, pos, true, s);
+}
+
+qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
+                                void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return qwen3_layer_decode_padded(L, x, y, batch, cache_lens, nullptr, nullptr, k_cache, v_cache, cache_capacity,
+                                     workspace, workspace_bytes, stream);
 }
 
 qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width, float eps,
