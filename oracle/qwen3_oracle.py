@@ -15,7 +15,8 @@ reproduced: the GPU path is judged against the exact result).  Sources:
          Q/K normalization, SwiGLU, The whole model.
   [L6]   "Transformer architectures: from BERT to diffusion, lesson 6"
          (xmarva.github.io), sections 3 Grouped-query attention, 4 Training
-         stability (QK-norm formula), 5 Qwen3 in PyTorch, 8 (prefix caching;
+         stability (QK-norm formula), 5 Qwen3 in PyTorch, 7 (sliding-window
+         attention, rolling buffer, attention sinks), 8 (prefix caching;
          batched generation of left-padded prompts).
   [CHK]  "Understand modern AI from the inside out" (Qwen3 layer checklist page),
          items on pre-norm order, q_norm/k_norm placement, rotate-half, scaling,
@@ -32,6 +33,7 @@ __all__ = [
     "gqa_causal_attention", "qk_norm_rope", "layer_prefill", "layer_prefill_rows",
     "layer_decode", "layer_prefill_cached", "stack_prefill",
     "padded_positions", "masked_attention", "layer_prefill_padded", "layer_decode_padded",
+    "window_mask", "layer_prefill_window", "RollingCache", "layer_decode_rolling", "layer_decode_window",
 ]
 
 
@@ -377,6 +379,116 @@ def layer_decode_padded(x, w, cfg, k_cache, v_cache, cache_lens, pad_starts, pad
         keys = np.concatenate([_f64(k_cache[b])[:, :n], khat], axis=1)
         vals = np.concatenate([_f64(v_cache[b])[:, :n], v], axis=1)
         attn = masked_attention(qhat, keys, vals, real[None, :])
+        x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
+        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
+        khat_new[b], v_new[b] = khat[:, 0], v[:, 0]
+    return y, khat_new, v_new
+
+
+# ----------------------------------------------------------------------------- local attention
+
+def window_mask(q_pos, k_pos, window, sinks=0):
+    """[L6 section 7]: in a local layer token i sees token j iff i - W < j <= i
+    (itself included); with attention sinks the first `sinks` tokens stay visible
+    to every later token (mask | (causal & j < sinks)).  window = 0 means global
+    (plain causal).  q_pos: [Tq], k_pos: [Tk] -> [Tq, Tk] booleans."""
+    qp = np.asarray(q_pos)[:, None]
+    kp = np.asarray(k_pos)[None, :]
+    causal = kp <= qp
+    if window <= 0:
+        return causal
+    return (causal & (qp - kp < window)) | (causal & (kp < sinks))
+
+
+def layer_prefill_window(x, w, cfg, window, sinks=0):
+    """Prefill at positions 0..T-1 with the banded mask of window_mask (the page's
+    "full causal cache and a banded mask").  x: [B, T, H] -> y [B, T, H],
+    khat [B, Hkv, T, D], v [B, Hkv, T, D] (the whole causal cache)."""
+    hsize, hq, hkv, d = _dims(cfg)
+    x = _f64(x)
+    bsz, t = x.shape[0], x.shape[1]
+    pos = np.arange(t, dtype=np.float64)
+    vis = window_mask(np.arange(t), np.arange(t), window, sinks)
+    y = np.empty_like(x)
+    khat_all = np.empty((bsz, hkv, t, d))
+    v_all = np.empty((bsz, hkv, t, d))
+    for b in range(bsz):
+        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
+        attn = masked_attention(qhat, khat, v, vis)
+        x1 = x[b] + attn.transpose(1, 0, 2).reshape(t, hq * d) @ _f64(w["o_proj"]).T
+        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
+        khat_all[b], v_all[b] = khat, v
+    return y, khat_all, v_all
+
+
+class RollingCache:
+    """[L6 section 7]: a rolling buffer of a local layer keeps at most W keys and
+    values and writes token i over the token that has just left the window (slot
+    i mod W); order does not matter, since each key carries its position in its
+    rotation.  With sinks, the first `sinks` tokens keep slots 0..sinks-1 and the
+    ring of W slots after them holds the other tokens (token i >= sinks goes to
+    slot sinks + (i - sinks) mod W), so the buffer always holds exactly the keys
+    window_mask lets the newest token see.  Per sequence: k, v [Hkv, sinks + W, D]."""
+
+    def __init__(self, hkv, d, window, sinks=0):
+        self.window, self.sinks = window, sinks
+        self.k = np.zeros((hkv, sinks + window, d))
+        self.v = np.zeros((hkv, sinks + window, d))
+        self.seen = 0
+
+    def slot(self, i):
+        return i if i < self.sinks else self.sinks + (i - self.sinks) % self.window
+
+    def add(self, k, v):
+        s = self.slot(self.seen)
+        self.k[:, s], self.v[:, s] = k, v
+        self.seen += 1
+        return min(self.seen, self.sinks + self.window)          # slots holding tokens
+
+
+def layer_decode_rolling(x, w, cfg, caches):
+    """One decode step per sequence on its RollingCache (the page's token-by-token
+    run "with a rolling buffer ... and no mask at all"): the new token sits at
+    position caches[b].seen, its key/value enter the buffer first, then it attends
+    every filled slot.  x: [B, 1, H]; caches: list of RollingCache (updated).
+    Returns y [B, 1, H]."""
+    hsize, hq, hkv, d = _dims(cfg)
+    x = _f64(x)
+    y = np.empty_like(x)
+    for b, cache in enumerate(caches):
+        pos = np.array([float(cache.seen)])
+        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
+        n = cache.add(khat[:, 0], v[:, 0])
+        attn = masked_attention(qhat, cache.k[:, :n], cache.v[:, :n], np.ones((1, n), dtype=bool))
+        x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
+        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
+    return y
+
+
+def layer_decode_window(x, w, cfg, k_cache, v_cache, cache_lens, window, sinks=0):
+    """One decode step per sequence on a full (linear) cache under the window mask:
+    the new token at position cache_lens[b] (slot cache_lens[b]) attends the cached
+    keys window_mask allows and itself.  Returns y [B,1,H], khat_new, v_new [B,Hkv,D]."""
+    hsize, hq, hkv, d = _dims(cfg)
+    x = _f64(x)
+    bsz = x.shape[0]
+    y = np.empty_like(x)
+    khat_new = np.empty((bsz, hkv, d))
+    v_new = np.empty((bsz, hkv, d))
+    for b in range(bsz):
+        p = int(cache_lens[b])
+        pos = np.array([float(p)])
+        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
+        keys = np.concatenate([_f64(k_cache[b])[:, :p], khat], axis=1)
+        vals = np.concatenate([_f64(v_cache[b])[:, :p], v], axis=1)
+        vis = window_mask([p], np.arange(p + 1), window, sinks)
+        attn = masked_attention(qhat, keys, vals, vis)
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
         h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])

@@ -507,6 +507,65 @@ def test_masked_attention_reduces_to_causal():
                                oracle.gqa_causal_attention(q, k, v, pos, pos), atol=1e-13)
 
 
+
+# ---------------------------------------------------------------- local layers (lesson 6, section 7)
+
+def test_window_mask_page_rule():
+    g = golden("sliding_window_mask.json")
+    for case in g["cases"]:
+        m = oracle.window_mask(np.arange(6), np.arange(6), case["window"], case["sinks"])
+        assert m.astype(int).tolist() == case["mask"], case
+
+
+@pytest.mark.parametrize("window,sinks", [(4, 0), (5, 2), (1, 0), (3, 3)])
+def test_banded_prefill_equals_rolling_buffer_decode(window, sinks):
+    # the page's check: the full causal cache with a banded mask and a token-by-token run with a
+    # rolling buffer (no mask at all) compute the same thing; here in float64 the two agree to
+    # rounding, and the buffer never holds more than sinks + window slots
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=41)
+    t = 13
+    x = si.layer_input(cfg, 2, t, seed=41)
+    banded, _, _ = oracle.layer_prefill_window(x, w, cfg, window, sinks)
+    caches = [oracle.RollingCache(2, 32, window, sinks) for _ in range(2)]
+    steps = np.concatenate([oracle.layer_decode_rolling(x[:, i:i + 1], w, cfg, caches) for i in range(t)], axis=1)
+    np.testing.assert_allclose(steps, banded, atol=1e-12)
+    assert caches[0].k.shape[1] == sinks + window and caches[0].seen == t
+
+
+def test_window_special_cases():
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=42)
+    x = si.layer_input(cfg, 1, 9, seed=42)
+    full = oracle.layer_prefill(x, w, cfg)["y"]
+    # a window as long as the text is global attention; window 0 means global
+    np.testing.assert_allclose(oracle.layer_prefill_window(x, w, cfg, 9)[0], full, atol=1e-12)
+    np.testing.assert_allclose(oracle.layer_prefill_window(x, w, cfg, 0)[0], full, atol=1e-12)
+    # window 1: every token sees only itself, so its attention output is its own value and the
+    # row is the layer on that token alone
+    y1 = oracle.layer_prefill_window(x, w, cfg, 1)[0]
+    for t in range(9):
+        np.testing.assert_allclose(y1[0, t], oracle.layer_prefill(x[:, t:t + 1], w, cfg)["y"][0, 0], atol=1e-12)
+    # the banded prefill leaves keys and values untouched (only the mask changes)
+    _, kb, vb = oracle.layer_prefill_window(x, w, cfg, 3, 1)
+    ref = oracle.layer_prefill(x, w, cfg)
+    np.testing.assert_allclose(kb, ref["khat"], atol=1e-12)
+    np.testing.assert_allclose(vb, ref["v"], atol=1e-12)
+
+
+def test_window_decode_on_full_cache_equals_banded_rows():
+    # decode with the window mask over a full cache continues the banded prefill
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=43)
+    t, window, sinks = 11, 4, 2
+    x = si.layer_input(cfg, 2, t, seed=43)
+    banded, kb, vb = oracle.layer_prefill_window(x, w, cfg, window, sinks)
+    _, kp, vp = oracle.layer_prefill_window(x[:, :t - 1], w, cfg, window, sinks)
+    y, kn, vn = oracle.layer_decode_window(x[:, t - 1:], w, cfg, kp, vp, [t - 1, t - 1], window, sinks)
+    np.testing.assert_allclose(y[:, 0], banded[:, t - 1], atol=1e-12)
+    np.testing.assert_allclose(kn, kb[:, :, t - 1], atol=1e-12)
+
+
 def test_stack_applies_final_norm_after_last_layer():
     cfg = tiny_cfg()
     ws = [si.layer_weights(cfg, layer=l, seed=17) for l in range(3)]
