@@ -214,6 +214,47 @@ qwen3_status qwen3_layer_decode_padded(qwen3_layer* layer, const void* x, void* 
                                        int32_t cache_capacity, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
+/* Local (sliding-window) layers ("Transformer architectures: from BERT to
+ * diffusion, lesson 6", section 7): token i attends token j iff
+ * i - window < j <= i, itself included, plus the first `sinks` tokens of its
+ * sequence (attention sinks; they stay visible to every later token).
+ * window = 0 means a global layer (plain causal attention; sinks ignored).
+ *
+ * Prefill with that banded mask on a linear cache: as qwen3_layer_prefill_at
+ * (start_positions may be NULL), keys and values of every token are cached at
+ * their slots as usual, only the attention mask changes.  Each query block
+ * visits only the key tiles of its window and the sink tiles, so the attention
+ * work grows with seq_len * window instead of seq_len^2.
+ * Errors: as qwen3_layer_prefill_at, plus INVALID_ARGUMENT for a negative
+ * window or sinks. */
+qwen3_status qwen3_layer_prefill_window(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                        int32_t seq_len, const int32_t* start_positions, int32_t window,
+                                        int32_t sinks, void* k_cache, void* v_cache, int32_t cache_capacity,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode of a local layer.  positions is a HOST array [batch]: the new token of
+ * sequence b sits at position positions[b] (the number of tokens it has seen).
+ *  - rolling = 0: a linear cache as in qwen3_layer_decode (positions[b] is the
+ *    cache length, the token goes to slot positions[b]); it attends the cached
+ *    keys of its window and the sinks.  Key splits wholly outside both are not
+ *    read at all.
+ *  - rolling = 1: a rolling buffer (section 7: at most window keys, each token
+ *    written over the one that has just left the window; here with `sinks`
+ *    fixed slots in front): cache_capacity must equal sinks + window; the token
+ *    goes to slot p below sinks and to slot sinks + (p - sinks) mod window above,
+ *    and attends every filled slot (min(p + 1, sinks + window) of them) with no
+ *    mask: the buffer holds exactly its visible keys.  positions[b] may exceed
+ *    cache_capacity.  Running a sequence token by token from an empty buffer
+ *    reproduces qwen3_layer_prefill_window (the page's banded-vs-rolling check).
+ * Errors: as qwen3_layer_decode (the free-slot rule applies to linear caches
+ * only), plus INVALID_ARGUMENT for a negative window or sinks, or rolling with
+ * window = 0 or cache_capacity != sinks + window. */
+qwen3_status qwen3_layer_decode_window(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                       const int32_t* positions, int32_t window, int32_t sinks,
+                                       int32_t rolling, void* k_cache, void* v_cache,
+                                       int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* RMSNorm of `rows` rows of `width` elements ("17. A modern architecture:
  * Qwen3", section RMSNorm): y = weight * x / sqrt(mean(x^2) + eps), reduced in
  * fp32.  x, weight and y all hold `dtype`; used for the final norm after a

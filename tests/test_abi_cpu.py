@@ -207,6 +207,31 @@ def test_decode_padded_validation_before_launch(layer):
     assert decode_padded(layer, [10], [0], [3], ws_bytes=100) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL
 
 
+
+def test_window_entry_points_validation_before_launch(layer):
+    L = nat.lib()
+    # negative window or sinks
+    assert L.qwen3_layer_prefill_window(layer, FAKE, FAKE, 1, 4, None, -1, 0, FAKE, FAKE, 16, FAKE, 1 << 30,
+                                        None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert L.qwen3_layer_prefill_window(layer, FAKE, FAKE, 1, 4, None, 8, -2, FAKE, FAKE, 16, FAKE, 1 << 30,
+                                        None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    # the banded prefill keeps the linear-cache rules
+    assert L.qwen3_layer_prefill_window(layer, FAKE, FAKE, 1, 17, None, 8, 0, FAKE, FAKE, 16, FAKE, 1 << 30,
+                                        None) == nat.QWEN3_ERR_OUT_OF_RANGE
+
+    def dec(pos, window, sinks, rolling, cap, ws_bytes=1 << 30):
+        arr = (ctypes.c_int32 * len(pos))(*pos)
+        return L.qwen3_layer_decode_window(layer, FAKE, FAKE, len(pos), arr, window, sinks, rolling, FAKE, FAKE, cap,
+                                           FAKE, ws_bytes, None)
+
+    assert dec([5], 0, 0, 1, 8) == nat.QWEN3_ERR_INVALID_ARGUMENT          # rolling without a window
+    assert dec([5], 8, 2, 1, 8) == nat.QWEN3_ERR_INVALID_ARGUMENT          # buffer is sinks + window = 10
+    assert dec([5], 8, -1, 0, 64) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert dec([64], 8, 2, 0, 64) == nat.QWEN3_ERR_OUT_OF_RANGE            # linear cache: no free slot
+    assert dec([40960], 8, 2, 1, 10) == nat.QWEN3_ERR_OUT_OF_RANGE         # position limit
+    assert dec([100], 8, 2, 1, 10, ws_bytes=100) == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL   # past the capacity is fine
+
+
 def test_rmsnorm_validation_and_status_strings():
     L = nat.lib()
     assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 4, 12, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_UNSUPPORTED

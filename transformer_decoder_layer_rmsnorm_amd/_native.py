@@ -26,7 +26,8 @@ QWEN3_BF16 = 1
 EXPORTED = (
     "qwen3_layer_create", "qwen3_layer_destroy", "qwen3_layer_workspace_size",
     "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_prefill_at",
-    "qwen3_layer_prefill_padded", "qwen3_layer_decode", "qwen3_layer_decode_padded",
+    "qwen3_layer_prefill_padded", "qwen3_layer_prefill_window", "qwen3_layer_decode",
+    "qwen3_layer_decode_padded", "qwen3_layer_decode_window",
     "qwen3_rmsnorm", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
     "qwen3_status_string", "qwen3_last_error",
 )
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
         "qwen3_layer_prefill_at": ([P, P, P, I32, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_layer_prefill_padded": ([P, P, P, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, I32, P,
                                         SZ, P], ctypes.c_int),
+        "qwen3_layer_prefill_window": ([P, P, P, I32, I32, ctypes.POINTER(I32), I32, I32, P, P, I32, P, SZ, P],
+                                       ctypes.c_int),
+        "qwen3_layer_decode_window": ([P, P, P, I32, ctypes.POINTER(I32), I32, I32, I32, P, P, I32, P, SZ, P],
+                                      ctypes.c_int),
         "qwen3_layer_decode": ([P, P, P, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_layer_decode_padded": ([P, P, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
                                        P, P, I32, P, SZ, P], ctypes.c_int),
@@ -204,6 +209,27 @@ class Layer:
         check(lib().qwen3_layer_decode(self._h, _ptr(x), _ptr(y), b, lens, _ptr(k_cache), _ptr(v_cache),
                                        k_cache.shape[2], _ptr(workspace), nbytes, _stream(stream)),
               "qwen3_layer_decode")
+
+    def prefill_window(self, x, y, k_cache, v_cache, workspace, window, sinks=0, start_positions=None,
+                       stream=None) -> None:
+        """Prefill of a local layer: banded mask of `window` tokens plus `sinks` attention sinks
+        (qwen3_layer_prefill_window)."""
+        b, t = x.shape[0], x.shape[1]
+        starts = None if start_positions is None else (ctypes.c_int32 * b)(*[int(v) for v in start_positions])
+        check(lib().qwen3_layer_prefill_window(self._h, _ptr(x), _ptr(y), b, t, starts, int(window), int(sinks),
+                                               _ptr(k_cache), _ptr(v_cache), k_cache.shape[2], _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)),
+              "qwen3_layer_prefill_window")
+
+    def decode_window(self, x, y, positions, k_cache, v_cache, workspace, window, sinks=0, rolling=False,
+                      stream=None) -> None:
+        """Decode of a local layer on a linear cache or a rolling buffer (qwen3_layer_decode_window)."""
+        b = x.shape[0]
+        pos = (ctypes.c_int32 * b)(*[int(v) for v in positions])
+        check(lib().qwen3_layer_decode_window(self._h, _ptr(x), _ptr(y), b, pos, int(window), int(sinks),
+                                              1 if rolling else 0, _ptr(k_cache), _ptr(v_cache), k_cache.shape[2],
+                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)), "qwen3_layer_decode_window")
 
     def set_profiling(self, enabled: bool) -> None:
         check(lib().qwen3_layer_set_profiling(self._h, 1 if enabled else 0), "qwen3_layer_set_profiling")

@@ -10,6 +10,9 @@
 // fully coalesced 1 KB; the per-key dot products are finished with a butterfly over the 16
 // lanes of a key that also splits the g heads across those lanes (log2(g) fewer exchanges).
 // Values are streamed the same way and accumulated per lane for its 8 features.
+// Local layers ("lesson 6", section 7): on a linear cache, splits wholly before the window start
+// (and after the sinks) write an empty partial without reading anything; on a rolling buffer
+// every filled slot is visible and nothing is masked.
 #include <type_traits>
 
 #include "common.hpp"
@@ -21,6 +24,13 @@ namespace {
 
 constexpr int HD = 128;
 constexpr int SK = kDecodeSplitKeys;  // keys per workgroup
+
+// Cache slots holding the keys of sequence b's new token: slots 0 .. P (P = cache length before
+// it, its own slot included), or every filled slot of a rolling buffer of a.cap slots.
+__device__ __forceinline__ int decode_kv_len(const AttnArgs& a, int b) {
+    const int p = seq_pos(a.pos, b);
+    return a.local.rolling ? min(p + 1, a.cap) : p + 1;
+}
 constexpr int KPW = SK / 4;           // keys per wave
 
 template <int CTRL>
@@ -78,11 +88,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
     const AttnArgs& a = p.a;
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kv_len = seq_pos(a.pos, b) + 1;
+    const int kv_len = decode_kv_len(a, b);
     const int key0 = split * SK;
     if (key0 >= kv_len) return;
     int pad_lo, pad_hi;   // left-padding slots of this sequence: never attended by the new token
     seq_pad(a.pos, b, pad_lo, pad_hi);
+    // local layer on a linear cache: keys before the window start are skipped, except sinks
+    const int win_lo = (a.local.window > 0 && !a.local.rolling) ? kv_len - a.local.window : 0;
+    const int sinks = win_lo > 0 ? a.local.sinks : 0;
+    if (key0 + SK <= win_lo && key0 >= sinks) {
+        // no visible key in this split: an empty partial (weight 0 in the merge)
+        const int S = p.splits;
+        for (int idx = threadIdx.x; idx < G * HD; idx += 256) {
+            const int h = idx / HD, d = idx % HD;
+            const int64_t row = ((int64_t)b * a.Hq + kvh * G + h) * S + split;
+            p.part_o[row * HD + d] = 0.f;
+            if (d == 0) {
+                p.part_ml[row * 2] = -INFINITY;
+                p.part_ml[row * 2 + 1] = 0.f;
+            }
+        }
+        return;
+    }
     const int nk = min(SK, kv_len - key0);
     const int dc = lane & 15, ks = lane >> 4;
 
@@ -113,7 +140,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
         }
         int head;
         const float sum = key_reduce<G>(s, lane, head);
-        const bool visible = (kk < nk) & ((key0 + kk < pad_lo) | (key0 + kk >= pad_hi));
+        const int key = key0 + kk;
+        const bool visible = (kk < nk) & ((key < pad_lo) | (key >= pad_hi)) & ((key >= win_lo) | (key < sinks));
         if ((dc & ((16 / G) - 1)) == 0) sP[kk * G + head] = visible ? sum : -INFINITY;
     }
     // the first value rows are requested now, so HBM stays busy through the softmax phase
@@ -216,7 +244,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     const AttnArgs& a = p.a;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int kv_len = seq_pos(a.pos, b) + 1;
+    const int kv_len = decode_kv_len(a, b);
     const int ns = (kv_len + SK - 1) / SK;
     const int64_t row0 = ((int64_t)b * a.Hq + h) * p.splits;
     const float* ml = p.part_ml + row0 * 2;

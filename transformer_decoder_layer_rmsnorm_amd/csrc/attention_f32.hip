@@ -23,9 +23,17 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
     const int b = (int)(gw / ((int64_t)a.T * a.Hq));
     const int kvh = h / (a.Hq / a.Hkv);
     const int D = a.D;
-    const int pos = seq_pos(a.pos, b) + t;   // the query's cache slot
+    int pos = seq_pos(a.pos, b) + t;          // the query's cache slot (linear cache)
     int pad_lo, pad_hi;                       // left-padding slots, seen only by themselves
     seq_pad(a.pos, b, pad_lo, pad_hi);
+    // local layer: keys pos - window < j <= pos and the first `sinks`; on a rolling buffer every
+    // filled slot (the query's own included) is visible
+    int win_lo = (a.local.window > 0) ? pos - a.local.window + 1 : 0;
+    if (a.local.rolling) {
+        pos = min(pos, a.cap - 1);
+        win_lo = 0;
+    }
+    const int sinks = a.local.sinks;
 
     const float* q = static_cast<const float*>(a.qhat) + (((int64_t)b * a.Hq + h) * a.T + t) * D;
     const float* kb = static_cast<const float*>(a.k_cache) + ((int64_t)b * a.Hkv + kvh) * a.cap * D;
@@ -36,6 +44,7 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(AttnArgs a) {
     float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
     for (int j = 0; j <= pos; ++j) {
         if (j >= pad_lo && j < pad_hi && j != pos) continue;
+        if (j < win_lo && j >= sinks) continue;
         const float* kr = kb + (int64_t)j * D;
         const float* vr = vb + (int64_t)j * D;
         const float s = wave_sum((in0 ? q0 * kr[lane] : 0.f) + (in1 ? q1 * kr[lane + 64] : 0.f)) * a.scale;

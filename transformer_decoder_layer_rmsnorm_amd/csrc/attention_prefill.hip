@@ -41,6 +41,11 @@
 //    above its queries skip their MFMAs.
 //  * Left-padded batches ("lesson 6", section 8): keys in a sequence's padding slots are masked
 //    for every query but their own token, on the tiles that overlap the padding run.
+//  * Local layers (section 7): a query at position i sees keys i - W < j <= i and the first
+//    `sinks` keys; a workgroup visits only the sink tiles and the tiles from its first query's
+//    window start on, so the work grows with T * W instead of T^2.
+//  * Padding and local masks are compiled into a separate instantiation (MASKED), used only when
+//    a call has either; the plain causal kernel carries none of that code.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -66,7 +71,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int HPW, int KS, bool PAD>
+template <int HPW, int KS, bool MASKED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void flash_prefill_kernel(AttnArgs a, float sl2,
                                                                                                    bool pair_tiles) {
     constexpr int WPH = 4 / (HPW * KS);
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     const int qw = q0 + wq * 32;
     const int pos0 = __builtin_amdgcn_readfirstlane(seq_pos(a.pos, b));
     int pad_lo = 0, pad_hi = 0;   // left-padding slots: attended by nobody but themselves
-    if constexpr (PAD) {
+    if constexpr (MASKED) {
         seq_pad(a.pos, b, pad_lo, pad_hi);
         pad_lo = __builtin_amdgcn_readfirstlane(pad_lo);
         pad_hi = __builtin_amdgcn_readfirstlane(pad_hi);
@@ -125,6 +130,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     const int my_pos = pos0 + qw + (lane & 31);
     const int wave_first = pos0 + qw;
     const int wave_last = pos0 + min(qw + 31, a.T - 1);
+    // Key tiles visited: all of them for a global layer; for a local one the sink tiles and then
+    // the tiles from the window start of the workgroup's first query on.
+    const int win = MASKED ? a.local.window : 0, sinks = MASKED ? a.local.sinks : 0;
+    int tw0 = 0, nsink_t = 0;
+    if (win > 0) {
+        tw0 = min(max(0, pos0 + q0 - win + 1) / KT, ntiles - 1);
+        nsink_t = min((sinks + KT - 1) / KT, tw0);
+    }
+    const int nvis = nsink_t + (ntiles - tw0);
+    auto tidx = [&](int u) { return u < nsink_t ? u : tw0 + (u - nsink_t); };
 
     // Q^T fragments (B operand): query qw + lane%32, d chunk 2s + lane/32.
     bf16x8 qf[8];
@@ -147,11 +162,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     int4v rk[CH], rv[CH];
     auto load_k = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) rk[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, st_off + (t * KT + 16 * j) * HD * 2, 0, 0);
+        for (int j = 0; j < CH; ++j) rk[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, st_off + (tidx(t) * KT + 16 * j) * HD * 2, 0, 0);
     };
     auto load_v = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) rv[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, st_off + (t * KT + 16 * j) * HD * 2, 0, 0);
+        for (int j = 0; j < CH; ++j) rv[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, st_off + (tidx(t) * KT + 16 * j) * HD * 2, 0, 0);
     };
     auto store_k = [&](int slot) {
         bf16* d = sK + slot * K_ELEMS + st_row * KP + st_ch * 8;
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 #pragma unroll
         for (int i = 0; i < NKB; ++i) {
             const int kb = (KS == 1) ? i : ph;
-            live[i] = (t * KT + kb * 32) <= wave_last;
+            live[i] = (tidx(t) * KT + kb * 32) <= wave_last;
             if (live[i]) {
                 const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP);
                 sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
@@ -201,8 +216,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
         }
     };
     auto softmax_pv = [&](int t, f32x16 (&sacc)[NKB], const bool (&live)[NKB]) {
-        const int k0 = t * KT;
-        if (k0 + KT - 1 > wave_first || (PAD && k0 < pad_hi && k0 + KT > pad_lo)) {
+        const int k0 = tidx(t) * KT;
+        if (k0 + KT - 1 > wave_first ||
+            (MASKED && ((k0 < pad_hi && k0 + KT > pad_lo) || (win > 0 && k0 <= wave_last - win)))) {
 #pragma unroll
             for (int i = 0; i < NKB; ++i) {
                 const int kb = (KS == 1) ? i : ph;
@@ -211,7 +227,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                     // branch-free select (bitwise, not short-circuit operators)
                     const bool masked =
-                        (key > my_pos) | (PAD & (key >= pad_lo) & (key < pad_hi) & (key != my_pos));
+                        (key > my_pos) | (MASKED & (((key >= pad_lo) & (key < pad_hi) & (key != my_pos)) |
+                                                    ((win > 0) & (my_pos - key >= win) & (key >= sinks))));
                     sacc[i][r] = masked ? -INFINITY : sacc[i][r];
                 }
             }
@@ -265,12 +282,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     };
     // one pipelined step: S of tile t+1 goes out before tile t's softmax and PV
     auto step = [&](int t, f32x16 (&cur)[NKB], const bool (&lcur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB]) {
-        if (t + 2 < ntiles) load_k(t + 2);
-        if (t + 1 < ntiles) load_v(t + 1);
-        if (t + 1 < ntiles) s_tile(t + 1, nxt, lnxt);
+        if (t + 2 < nvis) load_k(t + 2);
+        if (t + 1 < nvis) load_v(t + 1);
+        if (t + 1 < nvis) s_tile(t + 1, nxt, lnxt);
         softmax_pv(t, cur, lcur);
-        if (t + 2 < ntiles) store_k(t & 1);
-        if (t + 1 < ntiles) store_v((t + 1) & 1);
+        if (t + 2 < nvis) store_k(t & 1);
+        if (t + 1 < nvis) store_v((t + 1) & 1);
         __syncthreads();
     };
 
@@ -278,7 +295,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     load_v(0);
     store_k(0);
     store_v(0);
-    if (ntiles > 1) {
+    if (nvis > 1) {
         load_k(1);
         store_k(1);
     }
@@ -287,9 +304,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     f32x16 sa[NKB], sb[NKB];
     bool la[NKB], lb[NKB];
     s_tile(0, sa, la);
-    for (int t = 0; t < ntiles; t += 2) {
+    for (int t = 0; t < nvis; t += 2) {
         step(t, sa, la, sb, lb);
-        if (t + 1 >= ntiles) break;
+        if (t + 1 >= nvis) break;
         step(t + 1, sb, lb, sa, la);
     }
 
@@ -335,19 +352,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     }
 }
 
-template <bool PAD>
+template <bool MASKED>
 hipError_t launch_hpw(const AttnArgs& a, int hpw, bool split, dim3 grid, float scale_log2, bool pair_tiles,
                       hipStream_t stream) {
     if (hpw == 4)
-        flash_prefill_kernel<4, 1, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+        flash_prefill_kernel<4, 1, MASKED><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else if (hpw == 2 && split)
-        flash_prefill_kernel<2, 2, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+        flash_prefill_kernel<2, 2, MASKED><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else if (hpw == 2)
-        flash_prefill_kernel<2, 1, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+        flash_prefill_kernel<2, 1, MASKED><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else if (split)
-        flash_prefill_kernel<1, 2, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+        flash_prefill_kernel<1, 2, MASKED><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     else
-        flash_prefill_kernel<1, 1, PAD><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
+        flash_prefill_kernel<1, 1, MASKED><<<grid, NT, 0, stream>>>(a, scale_log2, pair_tiles);
     return hipGetLastError();
 }
 
@@ -369,9 +386,9 @@ hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) 
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
     const bool pair_tiles = wgs <= 512;   // two workgroups per CU on 256 CUs
-    // the padding-aware variant only when some sequence has left padding
-    const bool pad = a.pos.dev_pad != nullptr || a.pos.n_pad_inline > 0;
-    if (pad) return launch_hpw<true>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
+    // the masking variant only when some sequence has left padding or the layer is local
+    const bool masked = a.pos.dev_pad != nullptr || a.pos.n_pad_inline > 0 || a.local.window > 0;
+    if (masked) return launch_hpw<true>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
     return launch_hpw<false>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
 }
 

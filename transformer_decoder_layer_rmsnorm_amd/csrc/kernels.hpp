@@ -48,6 +48,20 @@ __device__ __forceinline__ int slot_position(int slot, int lo, int hi) {
     return slot < lo ? slot : (slot >= hi ? slot - (hi - lo) : max(lo - 1, 0));
 }
 
+// Local (sliding-window) attention ("lesson 6", section 7): token i sees token j iff
+// i - window < j <= i, plus the first `sinks` tokens (attention sinks); window 0 = global.
+// With `rolling`, a decode cache is a rolling buffer of sinks + window slots: token i lives in
+// slot i below `sinks` and in slot sinks + (i - sinks) mod window above, so the buffer holds
+// exactly the keys the newest token sees and no mask is needed.
+struct LocalAttn {
+    int32_t window;
+    int32_t sinks;
+    int32_t rolling;
+};
+__device__ __forceinline__ int rolling_slot(const LocalAttn& w, int pos) {
+    return pos < w.sinks ? pos : w.sinks + (pos - w.sinks) % w.window;
+}
+
 inline int dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -98,6 +112,7 @@ struct QkRopeArgs {
     void* k_cache;          // [B, Hkv, cap, D]
     void* v_cache;          // [B, Hkv, cap, D]
     SeqPositions pos;       // position (and cache slot) of token 0 of each sequence
+    LocalAttn local;        // rolling: the cache slot is rolling_slot(position)
     int B, T, Hq, Hkv, D, cap;
     float eps;
     double turns[64];       // omega_i / (2 pi) for pair i < D/2, omega_i = theta^(-2i/D), fp64
@@ -111,6 +126,7 @@ struct AttnArgs {
     const void* v_cache;    // [B, Hkv, cap, D]
     void* out;              // [B, T, Hq, D] (token-major rows of width Hq * D)
     SeqPositions pos;       // position of query 0 of each sequence
+    LocalAttn local;        // window / sinks mask; rolling decode caches
     int B, T, Hq, Hkv, D, cap;
     float scale;            // D^-1/2
 };

@@ -6,8 +6,9 @@
 // by all heads, applied after the reshape to heads and before RoPE; V is neither normalised
 // nor rotated.  Section Rotary position embeddings: omega_i = theta^(-2i/D), feature i is
 // paired with feature i + D/2 and the pair is turned by p * omega_i; keys enter the cache
-// already rotated.  The token's cache slot and its position differ only for left-padded
-// batches ("lesson 6", section 8: positions count a row's real tokens).
+// already rotated.  The token's cache slot and its position differ for left-padded batches
+// ("lesson 6", section 8: positions count a row's real tokens) and for rolling-buffer caches of
+// local layers (section 7: the token overwrites the one that just left the window).
 //
 // One 256-thread workgroup per token; the cos/sin of each rotation pair are computed once per
 // token from an angle formed in fp64 (p * omega_i / 2pi, reduced exactly to [-1/2, 1/2] turn,
@@ -33,10 +34,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
     const int D = a.D;
     const int half = D >> 1;
     const bool active = lane < half;
-    const int slot = seq_pos(a.pos, b) + t;  // cache slot of the token
+    const int lin = seq_pos(a.pos, b) + t;   // cache slot of the token in a linear cache
     int pad_lo, pad_hi;
     seq_pad(a.pos, b, pad_lo, pad_hi);
-    const int pos = slot_position(slot, pad_lo, pad_hi);   // RoPE position (real tokens before it)
+    const int pos = slot_position(lin, pad_lo, pad_hi);    // RoPE position (real tokens before it)
+    const int slot = a.local.rolling ? rolling_slot(a.local, pos) : lin;
 
     // cos / sin of p * omega_lane.  The angle is formed in fp64 in turns (p * omega / 2pi),
     // reduced exactly to [-1/2, 1/2] turn, and only then evaluated in fp32 on [-pi, pi].
@@ -121,10 +123,11 @@ __global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slot = lane >> 4;          // head slot within a group of four heads
     const int j = lane & 15;             // features 4j..4j+3 and 64+4j..64+4j+3
-    const int cslot = seq_pos(a.pos, b) + t;   // cache slot of the token
+    const int lin = seq_pos(a.pos, b) + t;     // cache slot of the token in a linear cache
     int pad_lo, pad_hi;
     seq_pad(a.pos, b, pad_lo, pad_hi);
-    const int pos = slot_position(cslot, pad_lo, pad_hi);
+    const int pos = slot_position(lin, pad_lo, pad_hi);
+    const int cslot = a.local.rolling ? rolling_slot(a.local, pos) : lin;
 
     float cs[4], sn[4], gq[8], gk[8];
 #pragma unroll

@@ -216,7 +216,8 @@ GemmArgs gemm(const void* a, std::initializer_list<const void*> b, std::initiali
 
 // The whole layer on M = B*T tokens.  `pos` gives the position of token 0 of each sequence.
 qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, void* kc, void* vc, int cap,
-                       char* ws, const Layout& lay, const SeqPositions& pos, bool decode, hipStream_t s) {
+                       char* ws, const Layout& lay, const SeqPositions& pos, const LocalAttn& local, bool decode,
+                       hipStream_t s) {
     const qwen3_config& c = L->cfg;
     const DType t = dt(c);
     const int M = B * T, H = c.hidden_size, D = c.head_dim, I = c.intermediate_size;
@@ -249,6 +250,7 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     qa.k_cache = kc;
     qa.v_cache = vc;
     qa.pos = pos;
+    qa.local = local;
     qa.B = B;
     qa.T = T;
     qa.Hq = Hq;
@@ -264,6 +266,7 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     aa.v_cache = vc;
     aa.out = attn;
     aa.pos = pos;
+    aa.local = local;
     aa.B = B;
     aa.T = T;
     aa.Hq = Hq;
@@ -396,10 +399,14 @@ qwen3_status qwen3_layer_workspace_layout(const qwen3_layer* L, int32_t batch, i
     return QWEN3_OK;
 }
 
-qwen3_status qwen3_layer_prefill_padded(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
-                                        const int32_t* start_positions, const int32_t* pad_lens, void* k_cache,
-                                        void* v_cache, int32_t cache_capacity, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+qwen3_status prefill_impl(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                          const int32_t* start_positions, const int32_t* pad_lens, const LocalAttn& local,
+                          void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     qwen3_status st = check_sizes(L, batch, seq_len, cache_capacity);
     if (st != QWEN3_OK) return st;
     if (!x || !y || !k_cache || !v_cache || !workspace)
@@ -459,27 +466,53 @@ qwen3_status qwen3_layer_prefill_padded(qwen3_layer* L, const void* x, void* y, 
             }
         }
     }
-    return run_layer(L, x, y, batch, seq_len, k_cache, v_cache, cache_capacity, ws, lay, pos, false, s);
+    return run_layer(L, x, y, batch, seq_len, k_cache, v_cache, cache_capacity, ws, lay, pos, local, false, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+qwen3_status qwen3_layer_prefill_padded(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                        const int32_t* start_positions, const int32_t* pad_lens, void* k_cache,
+                                        void* v_cache, int32_t cache_capacity, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    return prefill_impl(L, x, y, batch, seq_len, start_positions, pad_lens, LocalAttn{0, 0, 0}, k_cache, v_cache,
+                        cache_capacity, workspace, workspace_bytes, stream);
+}
+
+qwen3_status qwen3_layer_prefill_window(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
+                                        const int32_t* start_positions, int32_t window, int32_t sinks,
+                                        void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    if (window < 0 || sinks < 0)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "window (%d) and sinks (%d) must be non-negative", window, sinks);
+    return prefill_impl(L, x, y, batch, seq_len, start_positions, nullptr, LocalAttn{window, window > 0 ? sinks : 0, 0},
+                        k_cache, v_cache, cache_capacity, workspace, workspace_bytes, stream);
 }
 
 qwen3_status qwen3_layer_prefill_at(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
                                     const int32_t* start_positions, void* k_cache, void* v_cache,
                                     int32_t cache_capacity, void* workspace, size_t workspace_bytes, void* stream) {
-    return qwen3_layer_prefill_padded(L, x, y, batch, seq_len, start_positions, nullptr, k_cache, v_cache,
-                                      cache_capacity, workspace, workspace_bytes, stream);
+    return prefill_impl(L, x, y, batch, seq_len, start_positions, nullptr, LocalAttn{0, 0, 0}, k_cache, v_cache,
+                        cache_capacity, workspace, workspace_bytes, stream);
 }
 
 qwen3_status qwen3_layer_prefill(qwen3_layer* L, const void* x, void* y, int32_t batch, int32_t seq_len,
                                  void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    return qwen3_layer_prefill_padded(L, x, y, batch, seq_len, nullptr, nullptr, k_cache, v_cache, cache_capacity,
-                                      workspace, workspace_bytes, stream);
+    return prefill_impl(L, x, y, batch, seq_len, nullptr, nullptr, LocalAttn{0, 0, 0}, k_cache, v_cache,
+                        cache_capacity, workspace, workspace_bytes, stream);
 }
 
-qwen3_status qwen3_layer_decode_padded(qwen3_layer* L, const void* x, void* y, int32_t batch,
-                                       const int32_t* cache_lens, const int32_t* pad_starts, const int32_t* pad_lens,
-                                       void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+qwen3_status decode_impl(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
+                         const int32_t* pad_starts, const int32_t* pad_lens, const LocalAttn& local, void* k_cache,
+                         void* v_cache, int32_t cache_capacity, void* workspace, size_t workspace_bytes,
+                         void* stream) {
     qwen3_status st = check_sizes(L, batch, 1, cache_capacity);
     if (st != QWEN3_OK) return st;
     if (!x || !y || !k_cache || !v_cache || !workspace || !cache_lens)
@@ -491,7 +524,7 @@ qwen3_status qwen3_layer_decode_padded(qwen3_layer* L, const void* x, void* y, i
     bool any_pad = false;
     for (int b = 0; b < batch; ++b) {
         const int n = cache_lens[b];
-        if (n < 0 || n >= cache_capacity)
+        if (n < 0 || (!local.rolling && n >= cache_capacity))
             return fail(QWEN3_ERR_OUT_OF_RANGE, "cache_lens[%d] = %d leaves no free slot in a cache of %d", b, n,
                         cache_capacity);
         if (n >= L->cfg.max_position_embeddings)
@@ -538,14 +571,43 @@ qwen3_status qwen3_layer_decode_padded(qwen3_layer* L, const void* x, void* y, i
             pos.n_pad_inline = batch;
         }
     }
-    return run_layer(L, x, y, batch, 1, k_cache, v_cache, cache_capacity, ws, lay, pos, true, s);
+    return run_layer(L, x, y, batch, 1, k_cache, v_cache, cache_capacity, ws, lay, pos, local, true, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+qwen3_status qwen3_layer_decode_padded(qwen3_layer* L, const void* x, void* y, int32_t batch,
+                                       const int32_t* cache_lens, const int32_t* pad_starts, const int32_t* pad_lens,
+                                       void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return decode_impl(L, x, y, batch, cache_lens, pad_starts, pad_lens, LocalAttn{0, 0, 0}, k_cache, v_cache,
+                       cache_capacity, workspace, workspace_bytes, stream);
+}
+
+qwen3_status qwen3_layer_decode_window(qwen3_layer* L, const void* x, void* y, int32_t batch,
+                                       const int32_t* positions, int32_t window, int32_t sinks, int32_t rolling,
+                                       void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (window < 0 || sinks < 0)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "window (%d) and sinks (%d) must be non-negative", window, sinks);
+    if (rolling) {
+        if (window == 0) return fail(QWEN3_ERR_INVALID_ARGUMENT, "a rolling buffer needs a window > 0");
+        if ((int64_t)sinks + window != cache_capacity)
+            return fail(QWEN3_ERR_INVALID_ARGUMENT, "a rolling buffer holds sinks + window = %lld slots, not %d",
+                        (long long)sinks + window, cache_capacity);
+    }
+    const LocalAttn local{window, window > 0 ? sinks : 0, rolling ? 1 : 0};
+    return decode_impl(L, x, y, batch, positions, nullptr, nullptr, local, k_cache, v_cache, cache_capacity,
+                       workspace, workspace_bytes, stream);
 }
 
 qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
                                 void* k_cache, void* v_cache, int32_t cache_capacity, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-    return qwen3_layer_decode_padded(L, x, y, batch, cache_lens, nullptr, nullptr, k_cache, v_cache, cache_capacity,
-                                     workspace, workspace_bytes, stream);
+    return decode_impl(L, x, y, batch, cache_lens, nullptr, nullptr, LocalAttn{0, 0, 0}, k_cache, v_cache,
+                       cache_capacity, workspace, workspace_bytes, stream);
 }
 
 qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width, float eps,
