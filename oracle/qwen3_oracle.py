@@ -34,6 +34,7 @@ __all__ = [
     "layer_decode", "layer_prefill_cached", "stack_prefill",
     "padded_positions", "masked_attention", "layer_prefill_padded", "layer_decode_padded",
     "window_mask", "layer_prefill_window", "RollingCache", "layer_decode_rolling", "layer_decode_window",
+    "rope_rotate_pairs",
 ]
 
 
@@ -75,6 +76,28 @@ def rope_rotate(a, positions, omega):
     c, s = np.cos(angle), np.sin(angle)
     a1, a2 = a[..., :half], a[..., half:]
     return np.concatenate([a1 * c - a2 * s, a2 * c + a1 * s], axis=-1)
+
+
+def rope_rotate_pairs(a, positions, omega, rotary_dim=None, adjacent=False):
+    """RoPE with the pairing and extent as parameters [Q17 Rotary position
+    embeddings: "The pairing convention is part of the contract"; apply_rope's
+    partial rotation].  Only the first rotary_dim features are rotated (the rest
+    pass through unchanged); pair i of them is (i, i + rotary_dim/2) (split-half,
+    Qwen/Llama) or (2i, 2i+1) (adjacent, the original paper), each turned by
+    p * omega_i exactly as in rope_rotate."""
+    a = _f64(a)
+    r = a.shape[-1] if not rotary_dim else rotary_dim
+    rot, rest = a[..., :r], a[..., r:]
+    if adjacent:
+        angle = _f64(positions)[:, None] * _f64(omega)[None, :]
+        c, s = np.cos(angle), np.sin(angle)
+        x1, x2 = rot[..., 0::2], rot[..., 1::2]
+        out = np.empty_like(rot)
+        out[..., 0::2] = x1 * c - x2 * s
+        out[..., 1::2] = x2 * c + x1 * s
+    else:
+        out = rope_rotate(rot, positions, omega)
+    return np.concatenate([out, rest], axis=-1)
 
 
 def silu(z):
@@ -124,6 +147,21 @@ def _dims(cfg):
     return (cfg.hidden_size, cfg.num_attention_heads, cfg.num_key_value_heads, cfg.head_dim)
 
 
+def _rope_variant(cfg):
+    """(rotary_dim, adjacent pairs, position scale) of a config; the Qwen3 defaults are
+    (head_dim, False, 1): every feature rotated, split-half pairs, positions as they are.
+    [Q17 Rotary position embeddings: partial RoPE rotates only the first rotary_dim
+    features, frequencies theta^(-2i/rotary_dim); the pairing convention; exercise 3:
+    linear RoPE scaling multiplies the positions by a factor.]"""
+    r = getattr(cfg, "rotary_dim", 0) or cfg.head_dim
+    return r, bool(getattr(cfg, "rope_adjacent_pairs", False)), float(getattr(cfg, "rope_position_scale", 1.0))
+
+
+def _gain(cfg, g):
+    """[Q17 RMSNorm, parity detail 2]: zero-centred norms (Gemma, Qwen3.5) apply 1 + g."""
+    return (1.0 + _f64(g)) if getattr(cfg, "norm_unit_offset", False) else _f64(g)
+
+
 def qk_norm_rope(h, w, cfg, positions, with_q=True, with_kv=True):
     """Projections, per-head Q/K RMSNorm, then RoPE, for the tokens of one sequence.
 
@@ -136,15 +174,17 @@ def qk_norm_rope(h, w, cfg, positions, with_q=True, with_kv=True):
     _, hq, hkv, d = _dims(cfg)
     h = _f64(h)
     t = h.shape[0]
-    omega = rope_inv_freq(d, cfg.rope_theta)
+    r, adjacent, pscale = _rope_variant(cfg)
+    omega = rope_inv_freq(r, cfg.rope_theta)
+    ppos = _f64(positions) * pscale
     qhat = khat = v = None
     if with_q:
         q = (h @ _f64(w["q_proj"]).T).reshape(t, hq, d).transpose(1, 0, 2)
-        qhat = rope_rotate(rmsnorm(q, w["q_norm"], cfg.rms_norm_eps), positions, omega)
+        qhat = rope_rotate_pairs(rmsnorm(q, _gain(cfg, w["q_norm"]), cfg.rms_norm_eps), ppos, omega, r, adjacent)
     if with_kv:
         k = (h @ _f64(w["k_proj"]).T).reshape(t, hkv, d).transpose(1, 0, 2)
         v = (h @ _f64(w["v_proj"]).T).reshape(t, hkv, d).transpose(1, 0, 2)
-        khat = rope_rotate(rmsnorm(k, w["k_norm"], cfg.rms_norm_eps), positions, omega)
+        khat = rope_rotate_pairs(rmsnorm(k, _gain(cfg, w["k_norm"]), cfg.rms_norm_eps), ppos, omega, r, adjacent)
     return qhat, khat, v
 
 
@@ -160,13 +200,13 @@ def _layer_sequence(x, w, cfg, rows=None):
     t = x.shape[0]
     positions = np.arange(t, dtype=np.float64)
     rows = np.arange(t) if rows is None else np.asarray(rows, dtype=np.int64)
-    h = rmsnorm(x, w["input_layernorm"], cfg.rms_norm_eps)
+    h = rmsnorm(x, _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)
     _, khat, v = qk_norm_rope(h, w, cfg, positions, with_q=False)
     qhat, _, _ = qk_norm_rope(h[rows], w, cfg, positions[rows], with_kv=False)
     attn = gqa_causal_attention(qhat, khat, v, positions[rows], positions)   # [Hq, R, D]
     attn_flat = attn.transpose(1, 0, 2).reshape(rows.size, hq * d)
     x1 = x[rows] + attn_flat @ _f64(w["o_proj"]).T
-    h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+    h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
     gate = h2 @ _f64(w["gate_proj"]).T
     up = h2 @ _f64(w["up_proj"]).T
     act = silu(gate) * up
@@ -222,13 +262,13 @@ def layer_decode(x, w, cfg, k_cache, v_cache, cache_lens):
     for b in range(bsz):
         p = int(cache_lens[b])
         pos = np.array([float(p)])
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)          # [1, H]
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)          # [1, H]
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)                         # [*, 1, D]
         keys = np.concatenate([_f64(k_cache[b])[:, :p], khat], axis=1)     # [Hkv, p+1, D]
         vals = np.concatenate([_f64(v_cache[b])[:, :p], v], axis=1)
         attn = gqa_causal_attention(qhat, keys, vals, pos, np.arange(p + 1, dtype=np.float64))
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_new[b], v_new[b] = khat[:, 0], v[:, 0]
     return y, khat_new, v_new
@@ -257,13 +297,13 @@ def layer_prefill_cached(x, w, cfg, k_cache, v_cache, starts):
     for b in range(bsz):
         p0 = int(starts[b])
         pos = np.arange(p0, p0 + t, dtype=np.float64)
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)          # [T, H]
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)          # [T, H]
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)                         # [*, T, D]
         keys = np.concatenate([_f64(k_cache[b])[:, :p0], khat], axis=1)    # [Hkv, p0+T, D]
         vals = np.concatenate([_f64(v_cache[b])[:, :p0], v], axis=1)
         attn = gqa_causal_attention(qhat, keys, vals, pos, np.arange(p0 + t, dtype=np.float64))
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(t, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_new[b], v_new[b] = khat, v
     return y, khat_new, v_new
@@ -278,7 +318,7 @@ def stack_prefill(x, layer_weights, final_gain, cfg, round_between=None):
         h = layer_prefill(h, w, cfg)["y"]
         if round_between is not None:
             h = _f64(round_between(h))
-    return rmsnorm(h, final_gain, cfg.rms_norm_eps)
+    return rmsnorm(h, _gain(cfg, final_gain), cfg.rms_norm_eps)
 
 
 # ----------------------------------------------------------------------------- left padding
@@ -341,7 +381,7 @@ def layer_prefill_padded(x, w, cfg, k_cache, v_cache, starts, pads):
         real = _padded_real(p0, pad, p0 + t)                                  # [p0+T] slots
         pos_all = padded_positions(real).astype(np.float64)
         pos = pos_all[p0:]
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
         keys = np.concatenate([_f64(k_cache[b])[:, :p0], khat], axis=1)
         vals = np.concatenate([_f64(v_cache[b])[:, :p0], v], axis=1)
@@ -350,7 +390,7 @@ def layer_prefill_padded(x, w, cfg, k_cache, v_cache, starts, pads):
         visible = ((kslot <= qslot) & real[None, :]) | (kslot == qslot)
         attn = masked_attention(qhat, keys, vals, visible)
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(t, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_new[b], v_new[b] = khat, v
     return y, khat_new, v_new
@@ -374,13 +414,13 @@ def layer_decode_padded(x, w, cfg, k_cache, v_cache, cache_lens, pad_starts, pad
         n = int(cache_lens[b])
         real = np.append(_padded_real(int(pad_starts[b]), int(pad_lens[b]), n), True)   # [n+1]
         pos = np.array([float(padded_positions(real)[-1])])
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
         keys = np.concatenate([_f64(k_cache[b])[:, :n], khat], axis=1)
         vals = np.concatenate([_f64(v_cache[b])[:, :n], v], axis=1)
         attn = masked_attention(qhat, keys, vals, real[None, :])
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_new[b], v_new[b] = khat[:, 0], v[:, 0]
     return y, khat_new, v_new
@@ -414,11 +454,11 @@ def layer_prefill_window(x, w, cfg, window, sinks=0):
     khat_all = np.empty((bsz, hkv, t, d))
     v_all = np.empty((bsz, hkv, t, d))
     for b in range(bsz):
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
         attn = masked_attention(qhat, khat, v, vis)
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(t, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_all[b], v_all[b] = khat, v
     return y, khat_all, v_all
@@ -460,12 +500,12 @@ def layer_decode_rolling(x, w, cfg, caches):
     y = np.empty_like(x)
     for b, cache in enumerate(caches):
         pos = np.array([float(cache.seen)])
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
         n = cache.add(khat[:, 0], v[:, 0])
         attn = masked_attention(qhat, cache.k[:, :n], cache.v[:, :n], np.ones((1, n), dtype=bool))
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
     return y
 
@@ -483,14 +523,14 @@ def layer_decode_window(x, w, cfg, k_cache, v_cache, cache_lens, window, sinks=0
     for b in range(bsz):
         p = int(cache_lens[b])
         pos = np.array([float(p)])
-        h = rmsnorm(x[b], w["input_layernorm"], cfg.rms_norm_eps)
+        h = rmsnorm(x[b], _gain(cfg, w["input_layernorm"]), cfg.rms_norm_eps)
         qhat, khat, v = qk_norm_rope(h, w, cfg, pos)
         keys = np.concatenate([_f64(k_cache[b])[:, :p], khat], axis=1)
         vals = np.concatenate([_f64(v_cache[b])[:, :p], v], axis=1)
         vis = window_mask([p], np.arange(p + 1), window, sinks)
         attn = masked_attention(qhat, keys, vals, vis)
         x1 = x[b] + attn.transpose(1, 0, 2).reshape(1, hq * d) @ _f64(w["o_proj"]).T
-        h2 = rmsnorm(x1, w["post_attention_layernorm"], cfg.rms_norm_eps)
+        h2 = rmsnorm(x1, _gain(cfg, w["post_attention_layernorm"]), cfg.rms_norm_eps)
         y[b] = x1 + swiglu_mlp(h2, w["gate_proj"], w["up_proj"], w["down_proj"])
         khat_new[b], v_new[b] = khat[:, 0], v[:, 0]
     return y, khat_new, v_new

@@ -10,7 +10,8 @@ Recipe (the pages print no seeds, weights or data for this path):
   * projection matrices are N(0, 0.02^2), in the ``nn.Linear`` layout [out, in]
     (Qwen3 page, Qwen3Attention and SwiGLU classes),
   * every RMSNorm gain (input, post-attention, q_norm, k_norm, final) is
-    1 + N(0, 0.1^2), so that no gain makes a sub-layer vanish,
+    1 + N(0, 0.1^2), so that no gain makes a sub-layer vanish (for zero-centred
+    norms, which apply 1 + g, the stored g is N(0, 0.1^2)),
   * layer inputs are N(0, 1); a decode-time KV cache holds N(0, 1) keys and values,
   * bf16 workloads round each float32 draw to bf16 (round to nearest even), and
     both sides consume exactly those values.
@@ -46,6 +47,11 @@ class LayerConfig:
     rms_norm_eps: float = 1.0e-6
     max_position_embeddings: int = 40960
     dtype: str = "bf16"           # "bf16" or "f32": storage type of weights and activations
+    # RoPE / RMSNorm variants (the Qwen3 defaults leave all four off)
+    rotary_dim: int = 0           # features rotated per head; 0 = all of head_dim (partial RoPE)
+    rope_adjacent_pairs: bool = False   # pair (2i, 2i+1) instead of (i, i + rotary_dim/2)
+    rope_position_scale: float = 1.0    # linear RoPE scaling: angles use position * scale
+    norm_unit_offset: bool = False      # zero-centred RMSNorm gains: (1 + g)
 
 
 @dataclass(frozen=True)
@@ -116,7 +122,8 @@ def layer_weights(cfg: LayerConfig, layer: int = 0, seed: int = 0,
     for tid, (name, shape) in enumerate(weight_shapes(cfg).items()):
         g = _rng(seed, layer, tid)
         z = g.standard_normal(shape, dtype=np.float32)
-        a = 1.0 + gain_std * z if name in GAIN_NAMES else weight_std * z
+        centre = 0.0 if cfg.norm_unit_offset else 1.0      # zero-centred gains are stored as g
+        a = centre + gain_std * z if name in GAIN_NAMES else weight_std * z
         out[name] = _finish(a, cfg.dtype)
     return out
 

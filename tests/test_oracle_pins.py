@@ -566,6 +566,90 @@ def test_window_decode_on_full_cache_equals_banded_rows():
     np.testing.assert_allclose(kn, kb[:, :, t - 1], atol=1e-12)
 
 
+
+# ---------------------------------------------------------------- RoPE / RMSNorm variants (Qwen3 page)
+
+def test_rope_pairs_full_split_half_is_rope_rotate():
+    rng = np.random.default_rng(61)
+    a = rng.standard_normal((3, 7, 16))
+    pos = rng.integers(0, 5000, 7).astype(np.float64)
+    omega = oracle.rope_inv_freq(16, 1e6)
+    np.testing.assert_array_equal(oracle.rope_rotate_pairs(a, pos, omega), oracle.rope_rotate(a, pos, omega))
+
+
+def test_rope_adjacent_pairs_against_complex_library_routine():
+    # adjacent pairs (2i, 2i+1) are the natural complex pairing: torch.view_as_complex
+    rng = np.random.default_rng(62)
+    d, r = 32, 32
+    a = rng.standard_normal((2, 9, d))
+    pos = np.arange(9, dtype=np.float64) * 37.0
+    omega = oracle.rope_inv_freq(r, 1e4)
+    got = oracle.rope_rotate_pairs(a, pos, omega, r, adjacent=True)
+    z = torch.view_as_complex(torch.from_numpy(a.reshape(2, 9, d // 2, 2)).contiguous())
+    rot = torch.polar(torch.ones(9, d // 2, dtype=torch.float64),
+                      torch.from_numpy(pos)[:, None] * torch.from_numpy(omega)[None, :])
+    ref = torch.view_as_real(z * rot).reshape(2, 9, d).numpy()
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    # the two conventions differ (the page: a model is trained with exactly one), but are the same
+    # rotation up to the permutation that takes (2i, 2i+1) to (i, i + d/2)
+    split = oracle.rope_rotate_pairs(a, pos, omega, r)
+    assert np.abs(split - got).max() > 0.1
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    np.testing.assert_allclose(oracle.rope_rotate_pairs(a[..., perm], pos, omega, r)[..., np.argsort(perm)], got,
+                               atol=1e-12)
+
+
+def test_partial_rope_against_page_apply_rope():
+    # apply_rope rotates the first rotary_dim features (split-half within them, frequencies
+    # theta^(-2i/rotary_dim)) and passes the rest through; written here with torch.cat /
+    # rotate_half the way the page's function is described, in float64
+    rng = np.random.default_rng(63)
+    d, r = 256, 64
+    a = rng.standard_normal((2, 5, d))
+    pos = np.array([0, 1, 17, 1000, 40000], dtype=np.float64)
+    omega = oracle.rope_inv_freq(r, 1e6)
+    got = oracle.rope_rotate_pairs(a, pos, omega, r)
+    A = torch.from_numpy(a)
+    ang = torch.from_numpy(pos)[:, None] * torch.from_numpy(omega)[None, :]
+    ang = torch.cat((ang, ang), dim=-1)
+    x_rot, x_pass = A[..., :r], A[..., r:]
+    h1, h2 = x_rot.chunk(2, dim=-1)
+    ref = torch.cat((x_rot * ang.cos() + torch.cat((-h2, h1), dim=-1) * ang.sin(), x_pass), dim=-1).numpy()
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+    np.testing.assert_array_equal(got[..., r:], a[..., r:])
+
+
+def test_linear_rope_scaling_rescales_positions():
+    # linear scaling multiplies the positions by a factor: with factor 1/4, position 4p turns every
+    # pair exactly as position p does unscaled, i.e. every wavelength is 4x longer
+    cfg = tiny_cfg()
+    w = si.layer_weights(cfg, seed=64)
+    h = si.layer_input(cfg, 1, 6, seed=64)[0]
+    p = np.arange(6, dtype=np.float64) * 3
+    scaled = si.LayerConfig(**{**cfg.__dict__, "rope_position_scale": 0.25})
+    q1, k1, _ = oracle.qk_norm_rope(h, w, scaled, 4 * p)
+    q0, k0, _ = oracle.qk_norm_rope(h, w, cfg, p)
+    np.testing.assert_allclose(q1, q0, atol=1e-12)
+    np.testing.assert_allclose(k1, k0, atol=1e-12)
+
+
+def test_zero_centred_norm_is_the_standard_norm_with_shifted_gains():
+    # (1 + g) with g = gamma - 1 is gamma: the zero-centred layer with every gain shifted by -1
+    # equals the standard layer, for all four norms of the layer and the final norm
+    cfg = tiny_cfg()
+    zc = si.LayerConfig(**{**cfg.__dict__, "norm_unit_offset": True})
+    w = si.layer_weights(cfg, seed=65)
+    wz = {k: (v - 1.0 if k in si.GAIN_NAMES else v) for k, v in w.items()}
+    x = si.layer_input(cfg, 2, 7, seed=65)
+    np.testing.assert_allclose(oracle.layer_prefill(x, wz, zc)["y"], oracle.layer_prefill(x, w, cfg)["y"],
+                               atol=1e-12)
+    gain = si.final_norm_gain(cfg, seed=65)
+    np.testing.assert_allclose(oracle.stack_prefill(x, [wz], gain - 1.0, zc),
+                               oracle.stack_prefill(x, [w], gain, cfg), atol=1e-12)
+    # and the seeded draw of a zero-centred layer is centred on 0
+    assert abs(float(np.mean(si.layer_weights(zc, seed=65)["input_layernorm"]))) < 0.05
+
+
 def test_stack_applies_final_norm_after_last_layer():
     cfg = tiny_cfg()
     ws = [si.layer_weights(cfg, layer=l, seed=17) for l in range(3)]
