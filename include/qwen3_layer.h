@@ -61,6 +61,18 @@ typedef struct {
     double  rope_theta;               /* RoPE base: omega_i = theta^(-2i/D) */
     float   rms_norm_eps;             /* added to the mean square inside the root */
     qwen3_dtype dtype;                /* storage type of weights, activations and cache */
+    /* RoPE and RMSNorm variants ("17. A modern architecture: Qwen3", sections
+     * RMSNorm and Rotary position embeddings, and its exercises).  All zero gives
+     * Qwen3 itself. */
+    int32_t rotary_dim;               /* features rotated per head (partial RoPE: only the
+                                         first rotary_dim, frequencies theta^(-2i/rotary_dim),
+                                         the rest pass through); 0 = head_dim; even */
+    int32_t rope_adjacent_pairs;      /* 1: pair features (2i, 2i+1) (the original paper);
+                                         0: (i, i + rotary_dim/2) (split-half, Qwen/Llama) */
+    double  rope_position_scale;      /* linear RoPE scaling: angles use position * scale;
+                                         0 = 1 (no scaling) */
+    int32_t norm_unit_offset;         /* 1: zero-centred RMSNorm gains (Gemma, Qwen3.5): every
+                                         norm of the layer applies (1 + g) instead of g */
 } qwen3_config;
 
 /* Device pointers to one layer's tensors (parameter names of the Qwen3
@@ -107,7 +119,9 @@ typedef struct {
  * pointer not 16-byte aligned), UNSUPPORTED (Hq % Hkv != 0 - the pages raise
  * on it in Qwen3Attention; a dtype or head_dim the kernels lack: bf16 needs
  * head_dim 128, fp32 head_dim <= 128; bf16 widths H, I, Hq*D, Hkv*D must be
- * multiples of 128, 1/2/4/8 query heads per KV head). */
+ * multiples of 128, 1/2/4/8 query heads per KV head), INVALID_ARGUMENT also for
+ * an odd or out-of-range rotary_dim, a negative or non-finite
+ * rope_position_scale, or flags other than 0/1. */
 qwen3_status qwen3_layer_create(const qwen3_config* config, const qwen3_layer_weights* weights,
                                 qwen3_layer** out_layer);
 
@@ -262,6 +276,13 @@ qwen3_status qwen3_layer_decode_window(qwen3_layer* layer, const void* x, void* 
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, DEVICE. */
 qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width,
                            float eps, qwen3_dtype dtype, void* stream);
+
+/* As qwen3_rmsnorm, with the gain applied as (gain_offset + weight): 1 for the
+ * zero-centred final norm of a model whose layers set norm_unit_offset, 0 is
+ * qwen3_rmsnorm. */
+qwen3_status qwen3_rmsnorm_gain_offset(const void* x, const void* weight, void* y, int64_t rows,
+                                       int32_t width, float eps, float gain_offset, qwen3_dtype dtype,
+                                       void* stream);
 
 /* Per-kernel timing of prefill / decode calls made while profiling is on:
  * every launch is bracketed by two hipEvents on the call's stream. */

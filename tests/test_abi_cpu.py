@@ -61,6 +61,10 @@ def err():
     (dict(num_attention_heads=6, num_key_value_heads=4), nat.QWEN3_ERR_UNSUPPORTED),  # Hq % Hkv
     (dict(hidden_size=60), nat.QWEN3_ERR_UNSUPPORTED),
     (dict(head_dim=256), nat.QWEN3_ERR_UNSUPPORTED),
+    (dict(rotary_dim=31), nat.QWEN3_ERR_INVALID_ARGUMENT),          # odd rotated width
+    (dict(rotary_dim=34), nat.QWEN3_ERR_INVALID_ARGUMENT),          # wider than head_dim 32
+    (dict(rope_position_scale=-0.5), nat.QWEN3_ERR_INVALID_ARGUMENT),
+    (dict(rope_position_scale=float("inf")), nat.QWEN3_ERR_INVALID_ARGUMENT),
 ])
 def test_create_rejects_bad_f32_configs(change, status):
     cfg = si.LayerConfig(**{**si.TINY_F32.__dict__, **change})
@@ -78,6 +82,20 @@ def test_create_rejects_unsupported_bf16_configs(change, status):
     cfg = si.LayerConfig(**{**si.QWEN3_0P6B.__dict__, **change})
     st, _ = create(cfg)
     assert st == status, err()
+
+
+def test_create_accepts_rope_and_norm_variants():
+    for change in [dict(rotary_dim=16), dict(rope_adjacent_pairs=True), dict(rope_position_scale=0.25),
+                   dict(norm_unit_offset=True), dict(rotary_dim=0)]:
+        cfg = si.LayerConfig(**{**si.TINY_F32.__dict__, **change})
+        st, h = create(cfg)
+        assert st == nat.QWEN3_OK, (change, err())
+        nat.lib().qwen3_layer_destroy(h)
+    c = nat.make_config(si.TINY_F32)
+    c.rope_adjacent_pairs = 2
+    h = ctypes.c_void_p()
+    assert nat.lib().qwen3_layer_create(ctypes.byref(c), ctypes.byref(fake_weights()), ctypes.byref(h)) \
+        == nat.QWEN3_ERR_INVALID_ARGUMENT
 
 
 def test_create_rejects_null_and_misaligned_weights():
@@ -237,6 +255,10 @@ def test_rmsnorm_validation_and_status_strings():
     assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 4, 12, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_UNSUPPORTED
     assert L.qwen3_rmsnorm(None, FAKE, FAKE, 4, 16, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
     assert L.qwen3_rmsnorm(FAKE, FAKE, FAKE, 0, 16, 1e-6, nat.QWEN3_BF16, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert L.qwen3_rmsnorm_gain_offset(FAKE, FAKE, FAKE, 4, 12, 1e-6, 1.0, nat.QWEN3_BF16, None) \
+        == nat.QWEN3_ERR_UNSUPPORTED
+    assert L.qwen3_rmsnorm_gain_offset(FAKE, FAKE, FAKE, 4, 16, 1e-6, float("nan"), nat.QWEN3_BF16, None) \
+        == nat.QWEN3_ERR_INVALID_ARGUMENT
     for s in range(6):
         assert L.qwen3_status_string(s)
     assert "unknown" in L.qwen3_status_string(99).decode()

@@ -28,7 +28,7 @@ EXPORTED = (
     "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_prefill_at",
     "qwen3_layer_prefill_padded", "qwen3_layer_prefill_window", "qwen3_layer_decode",
     "qwen3_layer_decode_padded", "qwen3_layer_decode_window",
-    "qwen3_rmsnorm", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
+    "qwen3_rmsnorm", "qwen3_rmsnorm_gain_offset", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
     "qwen3_status_string", "qwen3_last_error",
 )
 
@@ -44,6 +44,8 @@ class Config(ctypes.Structure):
         ("num_key_value_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("intermediate_size", ctypes.c_int32), ("max_position_embeddings", ctypes.c_int32),
         ("rope_theta", ctypes.c_double), ("rms_norm_eps", ctypes.c_float), ("dtype", ctypes.c_int),
+        ("rotary_dim", ctypes.c_int32), ("rope_adjacent_pairs", ctypes.c_int32),
+        ("rope_position_scale", ctypes.c_double), ("norm_unit_offset", ctypes.c_int32),
     ]
 
 
@@ -97,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "qwen3_layer_decode_padded": ([P, P, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
                                        P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_rmsnorm": ([P, P, P, I64, I32, F32, ctypes.c_int, P], ctypes.c_int),
+        "qwen3_rmsnorm_gain_offset": ([P, P, P, I64, I32, F32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_layer_set_profiling": ([P, I32], ctypes.c_int),
         "qwen3_layer_read_profile": ([P, ctypes.POINTER(StageTime), I32, ctypes.POINTER(I32)], ctypes.c_int),
         "qwen3_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -131,7 +134,10 @@ def make_config(cfg) -> Config:
     """cfg: any object with the config.json field names (e.g. seeded_inputs.LayerConfig)."""
     return Config(cfg.hidden_size, cfg.num_attention_heads, cfg.num_key_value_heads, cfg.head_dim,
                   cfg.intermediate_size, cfg.max_position_embeddings, float(cfg.rope_theta),
-                  float(cfg.rms_norm_eps), QWEN3_BF16 if cfg.dtype == "bf16" else QWEN3_F32)
+                  float(cfg.rms_norm_eps), QWEN3_BF16 if cfg.dtype == "bf16" else QWEN3_F32,
+                  int(getattr(cfg, "rotary_dim", 0)), 1 if getattr(cfg, "rope_adjacent_pairs", False) else 0,
+                  float(getattr(cfg, "rope_position_scale", 1.0)),
+                  1 if getattr(cfg, "norm_unit_offset", False) else 0)
 
 
 class Layer:
@@ -241,9 +247,13 @@ class Layer:
         return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n.value)}
 
 
-def rmsnorm(x, weight, y, eps: float, stream=None) -> None:
+def rmsnorm(x, weight, y, eps: float, stream=None, gain_offset: float = 0.0) -> None:
     width = x.shape[-1]
     rows = x.numel() // width
     dtype = QWEN3_BF16 if x.dtype == torch.bfloat16 else QWEN3_F32
+    if gain_offset:
+        check(lib().qwen3_rmsnorm_gain_offset(_ptr(x), _ptr(weight), _ptr(y), rows, width, float(eps),
+                                              float(gain_offset), dtype, _stream(stream)), "qwen3_rmsnorm_gain_offset")
+        return
     check(lib().qwen3_rmsnorm(_ptr(x), _ptr(weight), _ptr(y), rows, width, float(eps), dtype, _stream(stream)),
           "qwen3_rmsnorm")

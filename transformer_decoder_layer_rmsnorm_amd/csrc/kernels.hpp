@@ -68,11 +68,12 @@ inline int dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
 // y[r, :] = g * x[r, :] / sqrt(mean(x[r, :]^2) + eps), fp32 reduction, one rounding.
 // x1 = x + sum_s part[s] (fp32, written), then y = g * x1 / rms(x1): the residual add of a
 // split-K projection fused with the following RMSNorm.  part holds `splits` slabs [rows, width].
+// goff: gain offset, 0 for the pages' gains, 1 for zero-centred gains applied as (1 + g).
 hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, int splits, float* x1,
                                    const void* g, void* y, DType yt, int64_t rows, int width, float eps,
-                                   hipStream_t stream);
+                                   float goff, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt,
-                          int64_t rows, int width, float eps, hipStream_t stream);
+                          int64_t rows, int width, float eps, float goff, hipStream_t stream);
 
 // ---------------------------------------------------------------- projections (C = A * B^T)
 enum class Epilogue : int {
@@ -115,7 +116,11 @@ struct QkRopeArgs {
     LocalAttn local;        // rolling: the cache slot is rolling_slot(position)
     int B, T, Hq, Hkv, D, cap;
     float eps;
-    double turns[64];       // omega_i / (2 pi) for pair i < D/2, omega_i = theta^(-2i/D), fp64
+    float goff;             // q_norm / k_norm gain offset (1 for zero-centred gains)
+    int rotary_dim;         // features rotated per head (== D unless partial RoPE)
+    int adjacent;           // 1: pairs (2i, 2i+1); 0: pairs (i, i + rotary_dim/2)
+    double turns[64];       // position scale * omega_i / (2 pi) for pair i < rotary_dim/2,
+                            // omega_i = theta^(-2i/rotary_dim), fp64
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
 

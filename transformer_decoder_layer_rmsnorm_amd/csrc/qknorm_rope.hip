@@ -18,7 +18,11 @@
 // bf16, D = 128: 16 lanes per head, four heads per wave instruction.  Lane j of a head owns
 // features 4j..4j+3 and their rotation partners 64+4j..64+4j+3 (8-byte loads and stores, the
 // rotation stays inside the lane) and the head's sum of squares is a 16-lane DPP reduction.
-// Other shapes: lane l of a wave owns the pair (l, l + D/2), one head per wave at a time.
+// Other shapes and the RoPE variants (partial rotation of the first rotary_dim features,
+// "apply_rope rotates only the first cos.shape[-1] features"; adjacent pairs (2i, 2i+1), the
+// original paper's convention; linear position scaling, folded into the frequency table;
+// zero-centred gains 1 + g): lane l of a wave owns one rotation pair, one head per wave at a
+// time.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,10 +44,18 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
     const int pos = slot_position(lin, pad_lo, pad_hi);    // RoPE position (real tokens before it)
     const int slot = a.local.rolling ? rolling_slot(a.local, pos) : lin;
 
+    // Lane l (< D/2) owns two features f0, f1: rotation pair l when l < rotary_dim/2 - (l, l + r/2)
+    // split-half or (2l, 2l+1) adjacent - and otherwise two features past rotary_dim, which are
+    // normalised but not rotated (partial RoPE).
+    const int rh = a.rotary_dim >> 1;
+    const bool rotates = lane < rh;
+    const int f0 = rotates ? (a.adjacent ? 2 * lane : lane) : a.rotary_dim + 2 * (lane - rh);
+    const int f1 = rotates ? (a.adjacent ? 2 * lane + 1 : lane + rh) : f0 + 1;
+
     // cos / sin of p * omega_lane.  The angle is formed in fp64 in turns (p * omega / 2pi),
     // reduced exactly to [-1/2, 1/2] turn, and only then evaluated in fp32 on [-pi, pi].
     float c = 1.f, s = 0.f;
-    if (active) {
+    if (active && rotates) {
         const double turns = (double)pos * a.turns[lane];
         const float r = (float)(turns - rint(turns)) * 6.283185307179586f;
         sincosf(r, &s, &c);
@@ -61,8 +73,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
             const int hs = hs0 + 4 * i;
             x0[i] = x1[i] = 0.f;
             if (active && hs < nheads) {
-                x0[i] = to_f32(src[hs * D + lane]);
-                x1[i] = to_f32(src[hs * D + lane + half]);
+                x0[i] = to_f32(src[hs * D + f0]);
+                x1[i] = to_f32(src[hs * D + f1]);
             }
         }
 #pragma unroll
@@ -73,8 +85,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
                 const int kh = hs - a.Hq - a.Hkv;
                 T* dst = static_cast<T*>(a.v_cache) + (((int64_t)b * a.Hkv + kh) * a.cap + slot) * D;
                 if (active) {
-                    dst[lane] = from_f32<T>(x0[i]);
-                    dst[lane + half] = from_f32<T>(x1[i]);
+                    dst[f0] = from_f32<T>(x0[i]);
+                    dst[f1] = from_f32<T>(x1[i]);
                 }
                 continue;
             }
@@ -83,8 +95,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
             const float ss = wave_sum(x0[i] * x0[i] + x1[i] * x1[i]);
             const float rstd = rsqrtf(ss / (float)D + a.eps);
             if (!active) continue;
-            const float n0 = to_f32(gain[lane]) * (x0[i] * rstd);
-            const float n1 = to_f32(gain[lane + half]) * (x1[i] * rstd);
+            const float n0 = (a.goff + to_f32(gain[f0])) * (x0[i] * rstd);
+            const float n1 = (a.goff + to_f32(gain[f1])) * (x1[i] * rstd);
             const float r0 = n0 * c - n1 * s;
             const float r1 = n1 * c + n0 * s;
             T* dst;
@@ -94,8 +106,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(QkRopeArgs a) {
                 const int kh = hs - a.Hq;
                 dst = static_cast<T*>(a.k_cache) + (((int64_t)b * a.Hkv + kh) * a.cap + slot) * D;
             }
-            dst[lane] = from_f32<T>(r0);
-            dst[lane + half] = from_f32<T>(r1);
+            dst[f0] = from_f32<T>(r0);
+            dst[f1] = from_f32<T>(r1);
         }
     }
 }
@@ -146,8 +158,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
         const bf16x4 k1 = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(a.k_norm) + 64 + 4 * j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            gq[e] = (float)q0[e]; gq[4 + e] = (float)q1[e];
-            gk[e] = (float)k0[e]; gk[4 + e] = (float)k1[e];
+            gq[e] = a.goff + (float)q0[e]; gq[4 + e] = a.goff + (float)q1[e];
+            gk[e] = a.goff + (float)k0[e]; gk[4 + e] = a.goff + (float)k1[e];
         }
     }
 
@@ -208,7 +220,9 @@ hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t strea
     const int64_t tokens = (int64_t)args.B * args.T;
     if (tokens <= 0) return hipSuccess;
     if (args.D > 128 || (args.D & 1)) return hipErrorInvalidValue;
-    if (t == DType::BF16 && args.D == 128)
+    if (args.rotary_dim > args.D || (args.rotary_dim & 1) || args.rotary_dim < 0) return hipErrorInvalidValue;
+    // the vectorised kernel covers the Qwen3 layout (all 128 features rotated, split-half pairs)
+    if (t == DType::BF16 && args.D == 128 && args.rotary_dim == 128 && !args.adjacent)
         qknorm_rope_d128_bf16<<<(unsigned)tokens, 256, 0, stream>>>(args);
     else if (t == DType::BF16)
         qknorm_rope_kernel<bf16><<<(unsigned)tokens, 256, 0, stream>>>(args);

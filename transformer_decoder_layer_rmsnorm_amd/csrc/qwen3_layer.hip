@@ -82,6 +82,15 @@ qwen3_status validate_config(const qwen3_config* c) {
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "rms_norm_eps must be non-negative and finite");
     if (c->dtype != QWEN3_F32 && c->dtype != QWEN3_BF16)
         return fail(QWEN3_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)c->dtype);
+    if (c->rotary_dim < 0 || c->rotary_dim > c->head_dim || (c->rotary_dim & 1))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "rotary_dim %d must be even and within [0, head_dim %d]",
+                    c->rotary_dim, c->head_dim);
+    if (c->rope_adjacent_pairs != 0 && c->rope_adjacent_pairs != 1)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "rope_adjacent_pairs must be 0 or 1");
+    if (c->norm_unit_offset != 0 && c->norm_unit_offset != 1)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "norm_unit_offset must be 0 or 1");
+    if (!(c->rope_position_scale >= 0.0) || !std::isfinite(c->rope_position_scale))
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "rope_position_scale must be non-negative and finite");
     if (c->num_attention_heads % c->num_key_value_heads)
         return fail(QWEN3_ERR_UNSUPPORTED, "num_attention_heads %d is not a multiple of num_key_value_heads %d",
                     c->num_attention_heads, c->num_key_value_heads);
@@ -231,6 +240,7 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     void* h2 = ws + lay.h2;
     void* act = ws + lay.act;
     const float eps = c.rms_norm_eps;
+    const float gain_off = c.norm_unit_offset ? 1.f : 0.f;
     auto proj = [&](const GemmArgs& g) {
         if (!bf) return launch_gemm_f32(g, s);
         return g.M <= 64 ? launch_gemv_bf16(g, s) : launch_gemm_bf16(g, s);
@@ -239,7 +249,7 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
 #define STAGE(name, expr)                                    \
     if ((st = run_stage(L, name, s, [&]() { return (expr); })) != QWEN3_OK) return st;
 
-    STAGE("rmsnorm_input", launch_rmsnorm(x, t, L->w.input_layernorm, h, t, M, H, eps, s));
+    STAGE("rmsnorm_input", launch_rmsnorm(x, t, L->w.input_layernorm, h, t, M, H, eps, gain_off, s));
     STAGE("gemm_qkv", proj(gemm(h, {L->w.q_proj, L->w.k_proj, L->w.v_proj}, {Hq * D, Hkv * D, Hkv * D}, qkv, nullptr,
                                 M, (Hq + 2 * Hkv) * D, H, Epilogue::Store)));
     QkRopeArgs qa{};
@@ -259,6 +269,9 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     qa.cap = cap;
     qa.eps = eps;
     std::memcpy(qa.turns, L->rope_turns, sizeof(qa.turns));
+    qa.goff = gain_off;
+    qa.rotary_dim = c.rotary_dim;
+    qa.adjacent = c.rope_adjacent_pairs;
     STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
     AttnArgs aa{};
     aa.qhat = qhat;
@@ -297,10 +310,11 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
         go.splits = so;
         STAGE("gemm_o_residual", launch_gemm_bf16(go, s));
         STAGE("rmsnorm_post", launch_residual_rmsnorm(x, t, part, so, static_cast<float*>(x1),
-                                                      L->w.post_attention_layernorm, h2, t, M, H, eps, s));
+                                                      L->w.post_attention_layernorm, h2, t, M, H, eps, gain_off, s));
     } else {
         STAGE("gemm_o_residual", proj(gemm(attn, {L->w.o_proj}, {H}, x1, x, M, H, Hq * D, Epilogue::ResidToF32)));
-        STAGE("rmsnorm_post", launch_rmsnorm(x1, DType::F32, L->w.post_attention_layernorm, h2, t, M, H, eps, s));
+        STAGE("rmsnorm_post",
+              launch_rmsnorm(x1, DType::F32, L->w.post_attention_layernorm, h2, t, M, H, eps, gain_off, s));
     }
     STAGE("gemm_gate_up_swiglu", proj(gemm(h2, {L->w.gate_proj, L->w.up_proj}, {I, I}, act, nullptr, M, I, H,
                                            Epilogue::SwiGLU)));
@@ -347,11 +361,15 @@ qwen3_status qwen3_layer_create(const qwen3_config* config, const qwen3_layer_we
     L->cfg = *config;
     L->w = *weights;
     // RoPE frequencies ("17. A modern architecture: Qwen3", Rotary position embeddings):
-    // omega_i = theta^(-2i/D), kept in fp64 and in turns for the kernel's exact range reduction.
+    // omega_i = theta^(-2i/r) over the r = rotary_dim rotated features, kept in fp64 and in turns
+    // for the kernel's exact range reduction; linear position scaling is folded in.
+    if (L->cfg.rotary_dim == 0) L->cfg.rotary_dim = config->head_dim;
+    if (L->cfg.rope_position_scale == 0.0) L->cfg.rope_position_scale = 1.0;
+    const int r = L->cfg.rotary_dim;
     for (int i = 0; i < 64; ++i)
-        L->rope_turns[i] = i < config->head_dim / 2
-                               ? std::pow(config->rope_theta, -2.0 * i / config->head_dim) / (2.0 * M_PI)
-                               : 0.0;
+        L->rope_turns[i] = i < r / 2 ? L->cfg.rope_position_scale * std::pow(config->rope_theta, -2.0 * i / r) /
+                                           (2.0 * M_PI)
+                                     : 0.0;
     *out_layer = L;
     return QWEN3_OK;
 }
@@ -612,6 +630,12 @@ qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t 
 
 qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width, float eps,
                            qwen3_dtype dtype, void* stream) {
+    return qwen3_rmsnorm_gain_offset(x, weight, y, rows, width, eps, 0.f, dtype, stream);
+}
+
+qwen3_status qwen3_rmsnorm_gain_offset(const void* x, const void* weight, void* y, int64_t rows, int32_t width,
+                                       float eps, float gain_offset, qwen3_dtype dtype, void* stream) {
+    if (!std::isfinite(gain_offset)) return fail(QWEN3_ERR_INVALID_ARGUMENT, "gain_offset must be finite");
     if (!x || !weight || !y) return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, weight and y must be non-NULL");
     if (rows <= 0 || width <= 0) return fail(QWEN3_ERR_INVALID_ARGUMENT, "rows and width must be positive");
     if (!aligned16(x) || !aligned16(weight) || !aligned16(y))
@@ -620,7 +644,8 @@ qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t r
     if (width % 8) return fail(QWEN3_ERR_UNSUPPORTED, "width must be a multiple of 8");
     if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(QWEN3_ERR_INVALID_ARGUMENT, "eps must be non-negative");
     const DType t = dtype == QWEN3_BF16 ? DType::BF16 : DType::F32;
-    const hipError_t e = launch_rmsnorm(x, t, weight, y, t, rows, width, eps, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_rmsnorm(x, t, weight, y, t, rows, width, eps, gain_offset,
+                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "rmsnorm: %s", hipGetErrorString(e));
     return QWEN3_OK;
 }

@@ -3,7 +3,8 @@
 // "17. A modern architecture: Qwen3", section RMSNorm: y_i = g_i x_i / sqrt(mean_j x_j^2 + eps),
 // mean of squares in fp32 whatever the storage type.  Here the normalised value is multiplied
 // by the gain in fp32 and rounded once to the output type (the page rounds to the input type
-// before the gain; the difference is below one output ulp).
+// before the gain; the difference is below one output ulp).  Zero-centred gains (the page's
+// parity detail 2: Gemma and the Qwen3.5 family store g and apply 1 + g) take goff = 1.
 //
 // Memory-bound: each row is read once (16-byte loads, kept in registers up to 4096 wide) and
 // written once.  Four rows per 256-thread workgroup.
@@ -19,7 +20,8 @@ namespace q3 {
 
 template <typename TX, typename TY, int MAXC>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, const TY* __restrict__ g,
-                                                      TY* __restrict__ y, int64_t rows, int width, float eps) {
+                                                      TY* __restrict__ y, int64_t rows, int width, float eps,
+                                                      float goff) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
                 float gv[8], o[8];
                 load8(g + c * 8, gv);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[i] = gv[i] * (v[j][i] * rstd);
+                for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
                 store8(yr + c * 8, o);
             }
         }
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
             load8(xr + c * 8, v);
             load8(g + c * 8, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = gv[i] * (v[i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[i] * rstd);
             store8(yr + c * 8, o);
         }
     }
@@ -73,10 +75,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
 
 template <typename TX, typename TY>
 static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
-                               hipStream_t s) {
+                               float goff, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
     rmsnorm_kernel<TX, TY, 8><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
-                                                   static_cast<TY*>(y), rows, width, eps);
+                                                   static_cast<TY*>(y), rows, width, eps, goff);
     return hipGetLastError();
 }
 
@@ -85,7 +87,7 @@ template <typename TX, typename TY>
 __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restrict__ x, const float* __restrict__ part,
                                                                int splits, float* __restrict__ x1,
                                                                const TY* __restrict__ g, TY* __restrict__ y,
-                                                               int64_t rows, int width, float eps) {
+                                                               int64_t rows, int width, float eps, float goff) {
     constexpr int MAXC = 8;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -119,36 +121,36 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
             float gv[8], o[8];
             load8(g + c * 8, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = gv[i] * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
             store8(y + off + c * 8, o);
         }
     }
 }
 
 hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, int splits, float* x1, const void* g,
-                                   void* y, DType yt, int64_t rows, int width, float eps, hipStream_t s) {
+                                   void* y, DType yt, int64_t rows, int width, float eps, float goff, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     if ((width & 7) || width > 8 * 8 * kWave || splits < 1) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (xt == DType::BF16 && yt == DType::BF16)
         residual_rmsnorm_kernel<bf16, bf16><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), part, splits, x1,
                                                                   static_cast<const bf16*>(g), static_cast<bf16*>(y),
-                                                                  rows, width, eps);
+                                                                  rows, width, eps, goff);
     else if (xt == DType::F32 && yt == DType::F32)
         residual_rmsnorm_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), part, splits, x1,
                                                                     static_cast<const float*>(g), static_cast<float*>(y),
-                                                                    rows, width, eps);
+                                                                    rows, width, eps, goff);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt, int64_t rows, int width,
-                          float eps, hipStream_t stream) {
+                          float eps, float goff, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
-    if (xt == DType::BF16 && yt == DType::BF16) return launch_typed<bf16, bf16>(x, g, y, rows, width, eps, stream);
-    if (xt == DType::F32 && yt == DType::BF16) return launch_typed<float, bf16>(x, g, y, rows, width, eps, stream);
-    if (xt == DType::F32 && yt == DType::F32) return launch_typed<float, float>(x, g, y, rows, width, eps, stream);
+    if (xt == DType::BF16 && yt == DType::BF16) return launch_typed<bf16, bf16>(x, g, y, rows, width, eps, goff, stream);
+    if (xt == DType::F32 && yt == DType::BF16) return launch_typed<float, bf16>(x, g, y, rows, width, eps, goff, stream);
+    if (xt == DType::F32 && yt == DType::F32) return launch_typed<float, float>(x, g, y, rows, width, eps, goff, stream);
     return hipErrorInvalidValue;
 }
 
