@@ -87,12 +87,21 @@ def profile_steps(torch, layer, fn, steps):
     return {k: v[1] / v[0] for k, v in prof.items()}     # average ms per launch
 
 
+# stages that run a GEMM of the table above with more work fused into its epilogue
+FUSED_ALIASES = {"gemm_qkv_qknorm_rope": "gemm_qkv"}
+
+
+def stage_flops(flops, stage):
+    return flops.get(stage, flops.get(FUSED_ALIASES.get(stage, ""), None))
+
+
 def kernel_table(avg_ms, flops):
     out = {}
     for k, ms in avg_ms.items():
         e = {"avg_ms": round(ms, 5)}
-        if k in flops:
-            tf = flops[k] / (ms * 1e-3) / 1e12
+        f = stage_flops(flops, k)
+        if f is not None:
+            tf = f / (ms * 1e-3) / 1e12
             e.update(tflops=round(tf, 1), frac_of_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
         out[k] = e
     return out
@@ -107,9 +116,9 @@ def bench_prefill(torch, si, nat, wl, steps, warmup, device):
     total = sum(flops.values())
     res = dict(ms_per_step=ms, tokens_per_s=wl.batch * wl.seq_len / (ms * 1e-3),
                layer_tflops=total / (ms * 1e-3) / 1e12, kernels=kernel_table(avg, flops))
-    dominant = max((k for k in avg if k in flops), key=lambda k: avg[k])
+    dominant = max((k for k in avg if stage_flops(flops, k) is not None), key=lambda k: avg[k])
     res["dominant"] = dominant
-    res["dominant_flops"] = flops[dominant]
+    res["dominant_flops"] = stage_flops(flops, dominant)
     res["dominant_ms"] = avg[dominant]
     layer.close()
     return res

@@ -116,8 +116,11 @@ __device__ __forceinline__ void write_tile(const DevGemm& p, const f32x16 (&acc)
     }
 }
 
-template <Epilogue EPI, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
+// Main loop of the register-prefetch kernel: accumulates the workgroup's tile (and K range, for
+// split-K) into acc and hands acc to `epi` with the tile's coordinates; smem is the kernel's LDS,
+// free for the epilogue once the loop has ended.
+template <Epilogue EPI, int BM, int BN, int WM, int WN, typename Epi>
+__device__ __forceinline__ void gemm_bf16_body(const DevGemm& p, bf16* smem, Epi&& epi) {
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
     constexpr int NT = WM * WN * 64;
     constexpr int TM = BM / WM, TN = BN / WN;        // wave tile
@@ -125,8 +128,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
     constexpr int CA = BM * 8 / NT, CB = BN * 8 / NT;  // 16-byte chunks staged per thread per slab
     static_assert(CA >= 1 && CB >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile vs threads");
     static_assert(!DUAL || TN % 64 == 0, "SwiGLU tiles need whole gate/up block pairs per wave");
-    __shared__ __attribute__((aligned(16))) bf16 sA[2 * BM * LP];
-    __shared__ __attribute__((aligned(16))) bf16 sB[2 * BN * LP];
+    bf16* sA = smem;
+    bf16* sB = smem + 2 * BM * LP;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -219,10 +222,121 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
         __syncthreads();
     }
 
-    DevGemm q = p;
-    if constexpr (EPI == Epilogue::PartialF32) q.out = static_cast<float*>(p.out) + (int64_t)split * p.M * p.N;
-    write_tile<EPI, BN, TM, TN, FM, FN>(q, acc, m0, tn, wm, wn, lane);
+    epi(acc, m0, tn, wm, wn, lane, split);
 }
+
+template <Epilogue EPI, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
+    constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BM * LP + 2 * BN * LP];
+    gemm_bf16_body<EPI, BM, BN, WM, WN>(p, smem, [&](const f32x16 (&acc)[FM][FN], int m0, int tn, int wm, int wn,
+                                                     int lane, int split) {
+        DevGemm q = p;
+        if constexpr (EPI == Epilogue::PartialF32) q.out = static_cast<float*>(p.out) + (int64_t)split * p.M * p.N;
+        write_tile<EPI, BN, TM, TN, FM, FN>(q, acc, m0, tn, wm, wn, lane);
+    });
+}
+
+// ------------------------------------------------------------------ QKV projection + QK-norm + RoPE
+// For 128 x 128 tiles, each output tile column block is exactly one head (head_dim 128) of the
+// q | k | v layout, so the epilogue can finish step 3 of the layer in place ("17. A modern
+// architecture: Qwen3", section Attention with grouped KV heads and Q/K normalization: per-head
+// RMSNorm of q and k over head_dim with one gain per projection, then rotate-half RoPE at the
+// token's position; v copied to the cache): the fp32 tile goes to LDS, then 16 lanes per token
+// row normalise, rotate and store it as qhat [B, Hq, T, D] or into the K / V cache slots.  The
+// q / k vectors are normalised from the fp32 accumulators (no bf16 rounding before the norm).
+__device__ __forceinline__ float dpp_row_f32(float x, int ctrl_sel) {
+    switch (ctrl_sel) {
+        case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
+        case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));
+        case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+        default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));
+    }
+}
+// sum over each 16-lane row of the wave (DPP: quad permutes, half-row and row mirrors)
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_row_f32(v, 0);
+    v += dpp_row_f32(v, 1);
+    v += dpp_row_f32(v, 2);
+    v += dpp_row_f32(v, 3);
+    return v;
+}
+
+__global__ __launch_bounds__(256) void gemm_qkv_qkrope_kernel(DevGemm p, QkRopeArgs a) {
+    constexpr int BM = 128, BN = 128, WM = 2, WN = 2, TM = 64, TN = 64, FM = 2, FN = 2, D = 128;
+    constexpr int TP = D + 8;   // fp32 tile pitch: rows r and r+4 of a store land 32 banks apart
+    __shared__ __attribute__((aligned(16))) bf16 smem[2 * BM * LP + 2 * BN * LP];
+    static_assert(BM * TP * 4 <= (int)sizeof(smem), "fp32 tile fits the main loop's LDS");
+    gemm_bf16_body<Epilogue::Store, BM, BN, WM, WN>(p, smem, [&](const f32x16 (&acc)[FM][FN], int m0, int tn,
+                                                                 int wm, int wn, int lane, int) {
+        float* tile = reinterpret_cast<float*>(smem);
+        // the main loop ended with a barrier: every wave is done reading its last k-slab
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    tile[row * TP + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
+                }
+        __syncthreads();
+        const int hs = tn;                 // head of this column block: q heads, k heads, v heads
+        const bool is_v = hs >= a.Hq + a.Hkv, is_q = hs < a.Hq;
+        const int jl = threadIdx.x & 15;   // features 4j..4j+3 and 64+4j..64+4j+3
+        float g[8];
+        if (!is_v) {
+            const bf16* gain = static_cast<const bf16*>(is_q ? a.q_norm : a.k_norm);
+            const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(gain + 4 * jl);
+            const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(gain + 64 + 4 * jl);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                g[e] = a.goff + (float)g0[e];
+                g[4 + e] = a.goff + (float)g1[e];
+            }
+        }
+        for (int row = threadIdx.x >> 4; row < BM; row += 16) {
+            const int m = m0 + row;
+            const bool valid = m < p.M;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + row * TP + 4 * jl);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + row * TP + 64 + 4 * jl);
+            const int b = valid ? m / a.T : 0, t = valid ? m - b * a.T : 0;
+            const int lin = seq_pos(a.pos, b) + t;
+            int pad_lo, pad_hi;
+            seq_pad(a.pos, b, pad_lo, pad_hi);
+            const int pos = slot_position(lin, pad_lo, pad_hi);
+            bf16x4 olo, ohi;
+            bf16* dst;
+            if (is_v) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { olo[e] = (bf16)lo[e]; ohi[e] = (bf16)hi[e]; }
+                dst = static_cast<bf16*>(a.v_cache) + (((int64_t)b * a.Hkv + (hs - a.Hq - a.Hkv)) * a.cap + lin) * D;
+            } else {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss = fmaf(lo[e], lo[e], fmaf(hi[e], hi[e], ss));
+                const float rstd = rsqrtf(sum16(ss) * (1.0f / D) + a.eps);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // angle in turns formed in fp64 and reduced exactly before the fp32 sin / cos
+                    const double turns = (double)pos * a.turns[4 * jl + e];
+                    const float rr = (float)(turns - rint(turns));
+                    const float sn = __builtin_amdgcn_sinf(rr), cs = __builtin_amdgcn_cosf(rr);
+                    const float n0 = g[e] * (lo[e] * rstd), n1 = g[4 + e] * (hi[e] * rstd);
+                    olo[e] = (bf16)(n0 * cs - n1 * sn);
+                    ohi[e] = (bf16)(n1 * cs + n0 * sn);
+                }
+                dst = is_q ? static_cast<bf16*>(a.qhat) + (((int64_t)b * a.Hq + hs) * a.T + t) * D
+                           : static_cast<bf16*>(a.k_cache) + (((int64_t)b * a.Hkv + (hs - a.Hq)) * a.cap + lin) * D;
+            }
+            if (valid) {
+                *reinterpret_cast<bf16x4*>(dst + 4 * jl) = olo;
+                *reinterpret_cast<bf16x4*>(dst + 64 + 4 * jl) = ohi;
+            }
+        }
+    });
+}
+
 
 // ------------------------------------------------------------------ large tiles, LDS DMA
 constexpr int DBK = 32;   // k per stage: one LDS row = 64 bytes = four 16-byte chunks
@@ -715,6 +829,26 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
         return run_tile<EPI, 64, 128, 2, 2>(p, s);
     else
         return run_tile<EPI, 64, 64, 2, 2>(p, s);
+}
+
+bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a) {
+    if (g.epi != Epilogue::Store || g.M <= 64 || a.D != 128 || a.rotary_dim != 128 || a.adjacent || a.local.rolling)
+        return false;
+    if (g.N != (a.Hq + 2 * a.Hkv) * 128 || g.N % 128 || g.K % BK) return false;
+    // the tiles the generic launcher would pick: 128 x 128 register tiles
+    const long tiles256 = (long)((g.M + 255) / 256) * (g.N / 256);
+    const long tiles128 = (long)((g.M + 127) / 128) * (g.N / 128);
+    return !(tiles256 >= 256 && g.N % 256 == 0) && tiles128 >= 256;
+}
+
+hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStream_t s) {
+    if (!gemm_qkv_fusable(g, a)) return hipErrorInvalidValue;
+    DevGemm p = make_dev(g);
+    p.splits = 1;
+    p.tiles_m = (p.M + 127) / 128;
+    p.tiles_n = p.N / 128;
+    gemm_qkv_qkrope_kernel<<<(unsigned)(p.tiles_m * p.tiles_n), 256, 0, s>>>(p, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {

@@ -123,6 +123,11 @@ struct QkRopeArgs {
                             // omega_i = theta^(-2i/rotary_dim), fp64
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
+// QKV projection with QK-norm + RoPE + cache write fused into its epilogue (bf16, head_dim 128,
+// full split-half RoPE, prefill shapes that take 128 x 128 tiles); `fusable` says whether the
+// combination applies, else the caller runs the GEMM and launch_qknorm_rope separately.
+bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a);
+hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

@@ -250,8 +250,6 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     if ((st = run_stage(L, name, s, [&]() { return (expr); })) != QWEN3_OK) return st;
 
     STAGE("rmsnorm_input", launch_rmsnorm(x, t, L->w.input_layernorm, h, t, M, H, eps, gain_off, s));
-    STAGE("gemm_qkv", proj(gemm(h, {L->w.q_proj, L->w.k_proj, L->w.v_proj}, {Hq * D, Hkv * D, Hkv * D}, qkv, nullptr,
-                                M, (Hq + 2 * Hkv) * D, H, Epilogue::Store)));
     QkRopeArgs qa{};
     qa.qkv = qkv;
     qa.q_norm = L->w.q_norm;
@@ -272,7 +270,16 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     qa.goff = gain_off;
     qa.rotary_dim = c.rotary_dim;
     qa.adjacent = c.rope_adjacent_pairs;
-    STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
+    // QKV projection; for prefill shapes on 128 x 128 tiles the QK-norm + RoPE + cache write runs
+    // in the GEMM's epilogue (one kernel), otherwise as its own kernel
+    const GemmArgs gq = gemm(h, {L->w.q_proj, L->w.k_proj, L->w.v_proj}, {Hq * D, Hkv * D, Hkv * D}, qkv, nullptr,
+                             M, (Hq + 2 * Hkv) * D, H, Epilogue::Store);
+    if (bf && gemm_qkv_fusable(gq, qa)) {
+        STAGE("gemm_qkv_qknorm_rope", launch_gemm_qkv_qkrope(gq, qa, s));
+    } else {
+        STAGE("gemm_qkv", proj(gq));
+        STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
+    }
     AttnArgs aa{};
     aa.qhat = qhat;
     aa.k_cache = kc;
