@@ -11,8 +11,8 @@
 // wave's LDS base + 16 l, without passing through VGPRs), BK = 32 per stage and four stages in
 // flight, so a k-slab is requested three stages before it is used.  LDS rows are unpadded 64-byte
 // rows whose four 16-byte chunks are XOR-swizzled by row, which keeps fragment reads free of bank
-// conflicts; each load instruction covers 16 rows of one operand.  For long K (>= 2048) a
-// ping-pong variant of the same tile is used instead: 64-k stages with 128-byte LDS rows (every
+// conflicts; each load instruction covers 16 rows of one operand.  Whenever K is a multiple of 64
+// a ping-pong variant of the same tile is used instead: 64-k stages with 128-byte LDS rows (every
 // load moves whole cache lines) and the two wave groups of each SIMD alternating between memory
 // and matrix phases (see gemm_bf16_pp_kernel).
 //
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dma_kernel(DevGemm p) 
 }
 
 
-// ------------------------------------------------------------------ large tiles, long K: ping-pong
+// ------------------------------------------------------------------ large tiles: ping-pong
 // 256 x 256 tiles on 8 waves (4 x 2, each wave 64 x 128), BK = 64 per stage in two LDS stages of
 // 128-byte rows (8 chunks of 16 bytes, XOR-swizzled by (row >> 1) & 7), so that every DMA
 // instruction moves 8 rows x 128 contiguous bytes: whole cache lines, which measurably lowers the
@@ -820,9 +820,11 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     const int bn256 = DUAL ? 128 : 256, bn128 = DUAL ? 64 : 128;
     const long tiles256 = (long)((p.M + 255) / 256) * (p.N / bn256);
     const long tiles128 = (long)((p.M + 127) / 128) * (p.N / bn128);
-    // long K: the ping-pong kernel (whole-line DMA, two 64-k stages); short K, where its
-    // two-stage fill and drain weigh more, the four-stage 32-k kernel
-    if (tiles256 >= 256 && p.N % bn256 == 0 && p.K % 64 == 0 && p.K >= 2048) return run_pp_tile<EPI>(p, s);
+    // 256 x 256 tiles: the ping-pong kernel (whole-line DMA, two 64-k stages) when K allows,
+    // else the four-stage 32-k kernel.  The ping-pong kernel is also taken with one tile for only
+    // three CUs in four: its per-tile rate outweighs the idle quarter (2048 x 6144 x 1024 SwiGLU
+    // product: 31.5 us against 38-40 us on 768 tiles of 128 x 128).
+    if (tiles256 >= 192 && p.N % bn256 == 0 && p.K % 64 == 0) return run_pp_tile<EPI>(p, s);
     if (tiles256 >= 256 && p.N % bn256 == 0) return run_dma_tile<EPI, 256, 256, 4, 2, 4>(p, s);
     if (tiles128 >= 256) return run_tile<EPI, 128, 128, 2, 2>(p, s);
     if constexpr (DUAL)
@@ -838,7 +840,7 @@ bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a) {
     // the tiles the generic launcher would pick: 128 x 128 register tiles
     const long tiles256 = (long)((g.M + 255) / 256) * (g.N / 256);
     const long tiles128 = (long)((g.M + 127) / 128) * (g.N / 128);
-    return !(tiles256 >= 256 && g.N % 256 == 0) && tiles128 >= 256;
+    return !(tiles256 >= 192 && g.N % 256 == 0) && tiles128 >= 256;
 }
 
 hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStream_t s) {
