@@ -134,6 +134,32 @@ def test_bf16_padded_many_sequences_values_in_workspace():
     assert_bf16_parity(to_np(yd), ref_d, f"padded decode y, {b} sequences")
 
 
+def test_bf16_padded_many_sequences_ping_pong_qkv_epilogue():
+    # 96 sequences x 32 tokens with Hq 16 / Hkv 8: the 3072 x 4096 QKV projection takes 256 x 256
+    # ping-pong tiles with the QK-norm / RoPE / cache-write epilogue, which reads the starts and
+    # the padding from the workspace arrays (more than 64 sequences)
+    cfg = small_bf16_cfg(hq=16, hkv=8)
+    gl = GpuLayer.seeded(cfg, seed=38)
+    b, t = 96, 32
+    pads = [(5 * i) % (t + 1) for i in range(b)]
+    starts = [(13 * i) % 29 for i in range(b)]
+    cap = max(starts) + t
+    log(f"bf16 padded prefill, {b} sequences x T{t}, Hq16 Hkv8 (ping-pong QKV epilogue)")
+    kc = np.zeros((b, 8, cap, 128), np.float32)
+    vc = np.zeros((b, 8, cap, 128), np.float32)
+    for i, n in enumerate(starts):
+        for h in range(8):
+            kc[i, h, :n] = si.cache_block(cfg, "k", i, h, n, seed=38)
+            vc[i, h, :n] = si.cache_block(cfg, "v", i, h, n, seed=38)
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    kc16, vc16 = to_np(kd), to_np(vd)
+    x = si.layer_input(cfg, b, t, seed=38)
+    y, kd, vd, _ = gl.prefill(to_dev(x, cfg), cap=cap, caches=(kd, vd), starts=starts, pads=pads)
+    ref, knew, vnew = oracle.layer_prefill_padded(x, gl.w_np, cfg, kc16, vc16, starts, pads)
+    assert_bf16_parity(to_np(y), ref, f"padded prefill y, {b} sequences")
+    _check_cache(to_np(kd), to_np(vd), knew, vnew, starts, t, "padded prefill (ping-pong epilogue)")
+
+
 def test_f32_padded_prefill_and_decode():
     cfg = si.TINY_F32
     gl = GpuLayer.seeded(cfg, seed=37)

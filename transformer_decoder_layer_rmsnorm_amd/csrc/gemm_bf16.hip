@@ -262,6 +262,95 @@ __device__ __forceinline__ float sum16(float v) {
     return v;
 }
 
+// Gains of head hs for the features lane jl handles (4jl..4jl+3 and 64+4jl..64+4jl+3).
+template <typename Args>
+__device__ __forceinline__ void qkrope_gains(const Args& a, int hs, int jl, float (&g)[8]) {
+    const bool is_v = hs >= a.Hq + a.Hkv, is_q = hs < a.Hq;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = 0.f;
+    if (is_v) return;
+    const void* qn = a.q_norm;
+    const void* kn = a.k_norm;
+    asm("" : "+s"(qn), "+s"(kn));   // select the loaded pointers, not the argument fields
+    const bf16* gain = static_cast<const bf16*>(is_q ? qn : kn);
+    const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(gain + 4 * jl);
+    const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(gain + 64 + 4 * jl);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        g[e] = a.goff + (float)g0[e];
+        g[4 + e] = a.goff + (float)g1[e];
+    }
+}
+
+// Arguments of the ping-pong variant: pointers and sizes only.  Its main loop is written with
+// memory-clobbering inline assembly, after which the compiler no longer reads a by-value kernel
+// argument in place but copies it to scratch memory when an array inside it is indexed at run
+// time; the arrays of QkRopeArgs are not needed here (angles and slots come from the table).
+struct QkPpArgs {
+    const void* q_norm;
+    const void* k_norm;
+    void* qhat;
+    void* k_cache;
+    void* v_cache;
+    const float* rope_cs;
+    const int32_t* rope_slot;
+    int T, Hq, Hkv, cap;
+    float eps, goff;
+};
+
+// Token row m of head hs (q, k or v column block of the QKV product), fp32 values at `tr`:
+// q and k are RMS-normalised over the head, scaled by their gains and rotated with the row's
+// (cos, sin) from the RoPE table, then stored to qhat or the K cache slot; v is rounded and
+// stored to the V cache slot.  The 16 lanes of a DPP row share the token; lane jl owns features
+// 4jl..4jl+3 and their rotation partners 64+4jl..64+4jl+3.  Every lane of the row takes part in
+// the reduction even when m >= M (its loads are clamped and its store is skipped).
+template <typename Args>
+__device__ __forceinline__ void qkrope_row(const float* tr, int jl, int m, int hs, const float (&g)[8],
+                                           const DevGemm& p, const Args& a) {
+    constexpr int D = 128;
+    // the argument's fields as values (selecting between fields would index the argument)
+    void* qhat = a.qhat;
+    void* kc = a.k_cache;
+    void* vc = a.v_cache;
+    int Hq = a.Hq, Hkv = a.Hkv;
+    asm("" : "+s"(qhat), "+s"(kc), "+s"(vc), "+s"(Hq), "+s"(Hkv));
+    const bool is_v = hs >= Hq + Hkv, is_q = hs < Hq;
+    const bool valid = m < p.M;
+    const int mc = valid ? m : p.M - 1;
+    const int b = mc / a.T, t = mc - b * a.T;
+    const int lin = a.rope_slot[mc];
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(tr + 4 * jl);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(tr + 64 + 4 * jl);
+    bf16x4 olo, ohi;
+    bf16* dst;
+    if (is_v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { olo[e] = (bf16)lo[e]; ohi[e] = (bf16)hi[e]; }
+        dst = static_cast<bf16*>(vc) + (((int64_t)b * Hkv + (hs - Hq - Hkv)) * a.cap + lin) * D;
+    } else {
+        const float* csr = a.rope_cs + (int64_t)mc * 128 + 8 * jl;   // (cos, sin) of 4jl..4jl+3
+        const f32x4 c01 = *reinterpret_cast<const f32x4*>(csr);
+        const f32x4 c23 = *reinterpret_cast<const f32x4*>(csr + 4);
+        const float cs[4] = {c01[0], c01[2], c23[0], c23[2]}, sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(lo[e], lo[e], fmaf(hi[e], hi[e], ss));
+        const float rstd = rsqrtf(sum16(ss) * (1.0f / D) + a.eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float n0 = g[e] * (lo[e] * rstd), n1 = g[4 + e] * (hi[e] * rstd);
+            olo[e] = (bf16)(n0 * cs[e] - n1 * sn[e]);
+            ohi[e] = (bf16)(n1 * cs[e] + n0 * sn[e]);
+        }
+        dst = is_q ? static_cast<bf16*>(qhat) + (((int64_t)b * Hq + hs) * a.T + t) * D
+                   : static_cast<bf16*>(kc) + (((int64_t)b * Hkv + (hs - Hq)) * a.cap + lin) * D;
+    }
+    if (valid) {
+        *reinterpret_cast<bf16x4*>(dst + 4 * jl) = olo;
+        *reinterpret_cast<bf16x4*>(dst + 64 + 4 * jl) = ohi;
+    }
+}
+
 __global__ __launch_bounds__(256) void gemm_qkv_qkrope_kernel(DevGemm p, QkRopeArgs a) {
     constexpr int BM = 128, BN = 128, WM = 2, WN = 2, TM = 64, TN = 64, FM = 2, FN = 2, D = 128;
     constexpr int TP = D + 8;   // fp32 tile pitch: rows r and r+4 of a store land 32 banks apart
@@ -281,59 +370,10 @@ __global__ __launch_bounds__(256) void gemm_qkv_qkrope_kernel(DevGemm p, QkRopeA
                     tile[row * TP + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
                 }
         __syncthreads();
-        const int hs = tn;                 // head of this column block: q heads, k heads, v heads
-        const bool is_v = hs >= a.Hq + a.Hkv, is_q = hs < a.Hq;
-        const int jl = threadIdx.x & 15;   // features 4j..4j+3 and 64+4j..64+4j+3
+        const int jl = threadIdx.x & 15;
         float g[8];
-        if (!is_v) {
-            const bf16* gain = static_cast<const bf16*>(is_q ? a.q_norm : a.k_norm);
-            const bf16x4 g0 = *reinterpret_cast<const bf16x4*>(gain + 4 * jl);
-            const bf16x4 g1 = *reinterpret_cast<const bf16x4*>(gain + 64 + 4 * jl);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                g[e] = a.goff + (float)g0[e];
-                g[4 + e] = a.goff + (float)g1[e];
-            }
-        }
-        for (int row = threadIdx.x >> 4; row < BM; row += 16) {
-            const int m = m0 + row;
-            const bool valid = m < p.M;
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(tile + row * TP + 4 * jl);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(tile + row * TP + 64 + 4 * jl);
-            const int b = valid ? m / a.T : 0, t = valid ? m - b * a.T : 0;
-            const int lin = seq_pos(a.pos, b) + t;
-            int pad_lo, pad_hi;
-            seq_pad(a.pos, b, pad_lo, pad_hi);
-            const int pos = slot_position(lin, pad_lo, pad_hi);
-            bf16x4 olo, ohi;
-            bf16* dst;
-            if (is_v) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { olo[e] = (bf16)lo[e]; ohi[e] = (bf16)hi[e]; }
-                dst = static_cast<bf16*>(a.v_cache) + (((int64_t)b * a.Hkv + (hs - a.Hq - a.Hkv)) * a.cap + lin) * D;
-            } else {
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ss = fmaf(lo[e], lo[e], fmaf(hi[e], hi[e], ss));
-                const float rstd = rsqrtf(sum16(ss) * (1.0f / D) + a.eps);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // angle in turns formed in fp64 and reduced exactly before the fp32 sin / cos
-                    const double turns = (double)pos * a.turns[4 * jl + e];
-                    const float rr = (float)(turns - rint(turns));
-                    const float sn = __builtin_amdgcn_sinf(rr), cs = __builtin_amdgcn_cosf(rr);
-                    const float n0 = g[e] * (lo[e] * rstd), n1 = g[4 + e] * (hi[e] * rstd);
-                    olo[e] = (bf16)(n0 * cs - n1 * sn);
-                    ohi[e] = (bf16)(n1 * cs + n0 * sn);
-                }
-                dst = is_q ? static_cast<bf16*>(a.qhat) + (((int64_t)b * a.Hq + hs) * a.T + t) * D
-                           : static_cast<bf16*>(a.k_cache) + (((int64_t)b * a.Hkv + (hs - a.Hq)) * a.cap + lin) * D;
-            }
-            if (valid) {
-                *reinterpret_cast<bf16x4*>(dst + 4 * jl) = olo;
-                *reinterpret_cast<bf16x4*>(dst + 64 + 4 * jl) = ohi;
-            }
-        }
+        qkrope_gains(a, tn, jl, g);   // the column block is head tn of the q | k | v layout
+        for (int row = threadIdx.x >> 4; row < BM; row += 16) qkrope_row(tile + row * TP, jl, m0 + row, tn, g, p, a);
     });
 }
 
@@ -516,14 +556,19 @@ __device__ __forceinline__ void vm_wait_at_most(int n) {
     else vm_wait<0>();
 }
 
-template <Epilogue EPI>
-__global__ __launch_bounds__(512) void gemm_bf16_pp_kernel(DevGemm p) {
-    constexpr int BM = 256, BN = 256, WN = 2, PK = 64;
-    constexpr int TM = 64, TN = 128, FM = 2, FN = 4;
+constexpr int kPpBM = 256, kPpBN = 256, kPpK = 64;
+constexpr int kPpTM = 64, kPpTN = 128, kPpFM = 2, kPpFN = 4;   // wave tile: 4 x 2 waves
+constexpr int kPpStage = kPpBM * kPpK;                         // elements per operand per stage
+
+// Main loop of the ping-pong kernel: accumulates the workgroup's 256 x 256 tile and hands acc to
+// `epi` with the tile's coordinates.  sA and sB are the kernel's LDS (2 stages each, 1 KB-aligned),
+// free for the epilogue once the loop has ended.
+template <Epilogue EPI, typename Epi>
+__device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* sB, Epi&& epi) {
+    constexpr int BM = kPpBM, BN = kPpBN, WN = 2, PK = kPpK;
+    constexpr int TM = kPpTM, TN = kPpTN, FM = kPpFM, FN = kPpFN;
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
-    constexpr int A_ST = BM * PK, B_ST = BN * PK;
-    __shared__ __attribute__((aligned(1024))) bf16 sA[2 * A_ST];
-    __shared__ __attribute__((aligned(1024))) bf16 sB[2 * B_ST];
+    constexpr int A_ST = kPpStage, B_ST = kPpStage;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -658,7 +703,57 @@ __global__ __launch_bounds__(512) void gemm_bf16_pp_kernel(DevGemm p) {
         }
     }
     if (grp == 0) barrier_only();
-    write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
+    epi(acc, m0, tn, wm, wn, lane);
+}
+
+template <Epilogue EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_pp_kernel(DevGemm p) {
+    __shared__ __attribute__((aligned(1024))) bf16 sA[2 * kPpStage];
+    __shared__ __attribute__((aligned(1024))) bf16 sB[2 * kPpStage];
+    gemm_pp_body<EPI>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][kPpFN], int m0, int tn, int wm, int wn, int lane) {
+        write_tile<EPI, kPpBN, kPpTM, kPpTN, kPpFM, kPpFN>(p, acc, m0, tn, wm, wn, lane);
+    });
+}
+
+// QKV projection on 256 x 256 ping-pong tiles with the QK-norm + RoPE + cache write epilogue
+// (same per-row work as gemm_qkv_qkrope_kernel).  A tile spans two heads, one per wave column
+// (wn), so the epilogue runs twice: the waves of column h put their fp32 accumulators for head
+// 2 tn + h into LDS (256 rows x 136 floats, over the stage buffers), then all 512 threads
+// finish its 256 token rows.
+constexpr int kPpQkTP = 128 + 8;
+__global__ __launch_bounds__(512) void gemm_qkv_qkrope_pp_kernel(DevGemm p, QkPpArgs a) {
+    constexpr int TP = kPpQkTP;
+    constexpr int SMEM = (kPpBM * TP * 4 > 4 * kPpStage * 2) ? kPpBM * TP * 4 : 4 * kPpStage * 2;
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    bf16* sA = reinterpret_cast<bf16*>(smem);
+    bf16* sB = sA + 2 * kPpStage;
+    gemm_pp_body<Epilogue::Store>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][kPpFN], int m0, int tn, int wm, int wn,
+                                                 int lane) {
+        float* tile = reinterpret_cast<float*>(smem);
+        const int jl = threadIdx.x & 15;
+        __syncthreads();   // every wave is past its last LDS fragment read
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            if (wn == hh) {
+#pragma unroll
+                for (int i = 0; i < kPpFM; ++i)
+#pragma unroll
+                    for (int j = 0; j < kPpFN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = wm * kPpTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                            tile[row * TP + j * 32 + (lane & 31)] = acc[i][j][r];
+                        }
+            }
+            __syncthreads();
+            const int hs = 2 * tn + hh;
+            float g[8];
+            qkrope_gains(a, hs, jl, g);
+#pragma unroll 1
+            for (int row = threadIdx.x >> 4; row < kPpBM; row += 32) qkrope_row(tile + row * TP, jl, m0 + row, hs, g, p, a);
+            __syncthreads();   // the tile is rewritten by the next head's waves
+        }
+    });
 }
 
 // ------------------------------------------------------------------ skinny (M <= 64)
@@ -833,23 +928,39 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
         return run_tile<EPI, 64, 64, 2, 2>(p, s);
 }
 
-bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a) {
+// Which fused QKV kernel serves the projection g (0: none): the tiles the generic launcher would
+// pick, 256 x 256 ping-pong (2) or 128 x 128 register tiles (1), provided each head is a whole
+// 128-column block and the RoPE is the plain rotate-half over the full head.
+static int qkv_fused_kind(const GemmArgs& g, const QkRopeArgs& a) {
     if (g.epi != Epilogue::Store || g.M <= 64 || a.D != 128 || a.rotary_dim != 128 || a.adjacent || a.local.rolling)
-        return false;
-    if (g.N != (a.Hq + 2 * a.Hkv) * 128 || g.N % 128 || g.K % BK) return false;
-    // the tiles the generic launcher would pick: 128 x 128 register tiles
+        return 0;
+    if (!a.rope_cs || !a.rope_slot || g.M != a.B * a.T) return 0;
+    if (g.N != (a.Hq + 2 * a.Hkv) * 128 || g.K % BK || g.K % kPpK) return 0;
     const long tiles256 = (long)((g.M + 255) / 256) * (g.N / 256);
     const long tiles128 = (long)((g.M + 127) / 128) * (g.N / 128);
-    return !(tiles256 >= 192 && g.N % 256 == 0) && tiles128 >= 256;
+    if (tiles256 >= 192 && g.N % 256 == 0) return (int64_t)g.K * 2 * 8 < ((int64_t)1 << 31) ? 2 : 0;
+    if (tiles256 >= 256 && g.N % 256 == 0) return 0;
+    return tiles128 >= 256 ? 1 : 0;
 }
 
+bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a) { return qkv_fused_kind(g, a) != 0; }
+
 hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStream_t s) {
-    if (!gemm_qkv_fusable(g, a)) return hipErrorInvalidValue;
+    const int kind = qkv_fused_kind(g, a);
+    if (kind == 0) return hipErrorInvalidValue;
     DevGemm p = make_dev(g);
     p.splits = 1;
-    p.tiles_m = (p.M + 127) / 128;
-    p.tiles_n = p.N / 128;
-    gemm_qkv_qkrope_kernel<<<(unsigned)(p.tiles_m * p.tiles_n), 256, 0, s>>>(p, a);
+    if (kind == 2) {
+        p.tiles_m = (p.M + kPpBM - 1) / kPpBM;
+        p.tiles_n = p.N / kPpBN;
+        const QkPpArgs pa{a.q_norm, a.k_norm, a.qhat, a.k_cache, a.v_cache, a.rope_cs, a.rope_slot,
+                          a.T, a.Hq, a.Hkv, a.cap, a.eps, a.goff};
+        gemm_qkv_qkrope_pp_kernel<<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p, pa);
+    } else {
+        p.tiles_m = (p.M + 127) / 128;
+        p.tiles_n = p.N / 128;
+        gemm_qkv_qkrope_kernel<<<(unsigned)(p.tiles_m * p.tiles_n), 256, 0, s>>>(p, a);
+    }
     return hipGetLastError();
 }
 

@@ -72,6 +72,22 @@ inline int dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
 hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, int splits, float* x1,
                                    const void* g, void* y, DType yt, int64_t rows, int width, float eps,
                                    float goff, hipStream_t stream);
+// RoPE angle table of a prefill call ("17. A modern architecture: Qwen3", section Rotary position
+// embeddings): for token row m = b T + t and frequency i < 64 (head_dim 128, rotate-half over
+// the whole head), cs[m][i] = (cos, sin) of 2 pi * turns[i] * position(m), the turn count formed
+// in fp64 and reduced to [-1/2, 1/2] before the fp32 sin / cos, and slot[m] = the row's cache
+// slot.  Written by the input RMSNorm (one row per wave, one frequency per lane) for the QKV
+// epilogue that rotates q and k and stores k and v.
+struct RopeTable {
+    float* cs;               // [rows, 64, 2] (cos, sin)
+    int32_t* slot;           // [rows] cache slot of each token row
+    SeqPositions pos;        // first slot and padding of each sequence
+    int T;                   // tokens per sequence
+    double turns[64];        // position scale * omega_i / (2 pi)
+};
+// bf16 input RMSNorm that also writes the RoPE table of its rows
+hipError_t launch_rmsnorm_rope(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
+                               float goff, const RopeTable& rope, hipStream_t stream);
 hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt,
                           int64_t rows, int width, float eps, float goff, hipStream_t stream);
 
@@ -121,10 +137,13 @@ struct QkRopeArgs {
     int adjacent;           // 1: pairs (2i, 2i+1); 0: pairs (i, i + rotary_dim/2)
     double turns[64];       // position scale * omega_i / (2 pi) for pair i < rotary_dim/2,
                             // omega_i = theta^(-2i/rotary_dim), fp64
+    const float* rope_cs;   // RopeTable::cs and ::slot of these rows, or nullptr (the fused QKV
+    const int32_t* rope_slot;  // epilogue needs them; launch_qknorm_rope works them out itself)
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
 // QKV projection with QK-norm + RoPE + cache write fused into its epilogue (bf16, head_dim 128,
-// full split-half RoPE, prefill shapes that take 128 x 128 tiles); `fusable` says whether the
+// full split-half RoPE, prefill shapes that take 128 x 128 register tiles or, with positions
+// that are zero or in device arrays, 256 x 256 ping-pong tiles); `fusable` says whether the
 // combination applies, else the caller runs the GEMM and launch_qknorm_rope separately.
 bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a);
 hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStream_t stream);

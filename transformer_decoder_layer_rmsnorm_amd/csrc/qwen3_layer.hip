@@ -249,7 +249,6 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
 #define STAGE(name, expr)                                    \
     if ((st = run_stage(L, name, s, [&]() { return (expr); })) != QWEN3_OK) return st;
 
-    STAGE("rmsnorm_input", launch_rmsnorm(x, t, L->w.input_layernorm, h, t, M, H, eps, gain_off, s));
     QkRopeArgs qa{};
     qa.qkv = qkv;
     qa.q_norm = L->w.q_norm;
@@ -270,11 +269,29 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     qa.goff = gain_off;
     qa.rotary_dim = c.rotary_dim;
     qa.adjacent = c.rope_adjacent_pairs;
-    // QKV projection; for prefill shapes on 128 x 128 tiles the QK-norm + RoPE + cache write runs
-    // in the GEMM's epilogue (one kernel), otherwise as its own kernel
+    // QKV projection; for prefill shapes (256 x 256 ping-pong or 128 x 128 register tiles) the
+    // QK-norm + RoPE + cache write runs in the GEMM's epilogue (one kernel), otherwise as its own
+    // kernel.  The fused epilogue reads each row's RoPE angles and cache slot from a table that
+    // the input RMSNorm writes into the x1 and h2 regions, which are free until o_proj.
     const GemmArgs gq = gemm(h, {L->w.q_proj, L->w.k_proj, L->w.v_proj}, {Hq * D, Hkv * D, Hkv * D}, qkv, nullptr,
                              M, (Hq + 2 * Hkv) * D, H, Epilogue::Store);
-    if (bf && gemm_qkv_fusable(gq, qa)) {
+    if (bf && !decode) {
+        qa.rope_cs = reinterpret_cast<const float*>(x1);
+        qa.rope_slot = reinterpret_cast<const int32_t*>(h2);
+    }
+    const bool fused_qkv = bf && !decode && gemm_qkv_fusable(gq, qa);
+    if (fused_qkv) {
+        RopeTable rt{};
+        rt.cs = static_cast<float*>(x1);
+        rt.slot = static_cast<int32_t*>(h2);
+        rt.pos = pos;
+        rt.T = T;
+        std::memcpy(rt.turns, L->rope_turns, sizeof(rt.turns));
+        STAGE("rmsnorm_input", launch_rmsnorm_rope(x, L->w.input_layernorm, h, M, H, eps, gain_off, rt, s));
+    } else {
+        STAGE("rmsnorm_input", launch_rmsnorm(x, t, L->w.input_layernorm, h, t, M, H, eps, gain_off, s));
+    }
+    if (fused_qkv) {
         STAGE("gemm_qkv_qknorm_rope", launch_gemm_qkv_qkrope(gq, qa, s));
     } else {
         STAGE("gemm_qkv", proj(gq));

@@ -73,6 +73,62 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
     }
 }
 
+// Input RMSNorm (bf16, width <= 4096) plus the RoPE table row of each token: lane i of the
+// row's wave forms the angle of frequency i (see RopeTable).
+__global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restrict__ x, const bf16* __restrict__ g,
+                                                           bf16* __restrict__ y, int64_t rows, int width, float eps,
+                                                           float goff, RopeTable rope) {
+    constexpr int MAXC = 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const bf16* xr = x + row * width;
+    bf16* yr = y + row * width;
+    const int nchunk = width >> 3;
+    float v[MAXC][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+        const int c = lane + j * kWave;
+        if (c < nchunk) {
+            load8(xr + c * 8, v[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+        }
+    }
+    // the angle of frequency `lane` at this token's position, while the loads are in flight
+    const int b = (int)(row / rope.T), t = (int)(row - (int64_t)b * rope.T);
+    const int lin = seq_pos(rope.pos, b) + t;
+    int pad_lo, pad_hi;
+    seq_pad(rope.pos, b, pad_lo, pad_hi);
+    const double turns = (double)slot_position(lin, pad_lo, pad_hi) * rope.turns[lane];
+    const float rr = (float)(turns - rint(turns));
+    const float2 cs = make_float2(__builtin_amdgcn_cosf(rr), __builtin_amdgcn_sinf(rr));
+    reinterpret_cast<float2*>(rope.cs)[row * 64 + lane] = cs;
+    if (lane == 0) rope.slot[row] = lin;
+    const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) {
+        const int c = lane + j * kWave;
+        if (c < nchunk) {
+            float gv[8], o[8];
+            load8(g + c * 8, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+            store8(yr + c * 8, o);
+        }
+    }
+}
+
+hipError_t launch_rmsnorm_rope(const void* x, const void* g, void* y, int64_t rows, int width, float eps, float goff,
+                               const RopeTable& rope, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if ((width & 7) || width > 8 * 8 * kWave || rope.T <= 0 || !rope.cs || !rope.slot) return hipErrorInvalidValue;
+    rmsnorm_rope_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g),
+                                                                   static_cast<bf16*>(y), rows, width, eps, goff, rope);
+    return hipGetLastError();
+}
+
 template <typename TX, typename TY>
 static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
                                float goff, hipStream_t s) {
