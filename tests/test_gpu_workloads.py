@@ -67,6 +67,23 @@ def test_qwen3_8b_layer_prefill_ragged_tail_rows():
     assert_bf16_parity(to_np(y)[0, ts], ref, f"y at {len(ts)} rows incl. the 40-row tail")
 
 
+def test_qwen3_0p6b_layer_prefill_ragged_tail_rows():
+    """0.6B shapes at T = 2088 (32 whole 64-row tiles plus a 40-row tail): down_proj takes the
+    64 x 64 register tiles, gate/up the ping-pong tiles, QKV the fused 128 x 128 kernel and
+    o_proj the split-K tiles, all with a partial last row tile; rows in and around the tail are
+    checked."""
+    wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
+    cfg = wl.cfg
+    t_len = 2088
+    log(f"0.6B-shaped layer: B1 T{t_len}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed)
+    x = si.layer_input(cfg, 1, t_len, seed=wl.seed)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    ts = [0, 63, 64, 1000, 2047, 2048, 2049, 2070, 2086, 2087]
+    ref = oracle.layer_prefill_rows(x, gl.w_np, cfg, [(0, t) for t in ts])
+    assert_bf16_parity(to_np(y)[0, ts], ref, f"y at {len(ts)} rows incl. the 40-row tail")
+
+
 def test_qwen3_8b_decode_32k_every_row():
     wl = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
     cfg = wl.cfg
