@@ -27,8 +27,8 @@
 // at a time for L2 reuse of the weight tiles.
 //
 // Skinny kernel (decode, M <= 64): v_mfma_f32_16x16x32_bf16 with the weight rows streamed
-// straight from HBM into B fragments; each workgroup owns 16 output columns and splits K
-// across its waves, reducing through LDS.
+// straight from HBM into B fragments; each workgroup owns 16 output columns and deals K out to
+// its waves in interleaved 32-k chunks, reducing through LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -764,8 +764,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
     __shared__ float red[NB][NW][MG][256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16;
-    const int kper = p.K / NW;
-    const int k0 = wave * kper + 8 * (lane >> 4);
+    // the waves take interleaved 32-k chunks, so a workgroup reads its 16 weight rows as runs of
+    // NW * 64 contiguous bytes (whole cache lines) rather than NW distant 64-byte pieces
+    const int k0 = wave * 32 + 8 * (lane >> 4);
 
     const bf16* brow[NB];
     if constexpr (DUAL) {
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
 
     const bf16x8 zero = {};
 #pragma unroll 4
-    for (int k = k0; k < wave * kper + kper; k += 32) {
+    for (int k = k0; k < p.K; k += 32 * NW) {
         bf16x8 bv[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const bf16x8*>(brow[nb] + k);

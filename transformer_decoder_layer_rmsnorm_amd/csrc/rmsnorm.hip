@@ -30,13 +30,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
     const int nchunk = width >> 3;   // chunks of 8 elements
 
     if (MAXC > 0 && nchunk <= MAXC * kWave) {
-        float v[MAXC][8];
+        // the gains are requested with the row, so a few-row call waits for one round trip
+        float v[MAXC][8], gv[MAXC][8];
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < MAXC; ++j) {
             const int c = lane + j * kWave;
             if (c < nchunk) {
                 load8(xr + c * 8, v[j]);
+                load8(g + c * 8, gv[j]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
             }
@@ -46,10 +48,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
         for (int j = 0; j < MAXC; ++j) {
             const int c = lane + j * kWave;
             if (c < nchunk) {
-                float gv[8], o[8];
-                load8(g + c * 8, gv);
+                float o[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+                for (int i = 0; i < 8; ++i) o[i] = (goff + gv[j][i]) * (v[j][i] * rstd);
                 store8(yr + c * 8, o);
             }
         }
@@ -85,13 +86,14 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
     const bf16* xr = x + row * width;
     bf16* yr = y + row * width;
     const int nchunk = width >> 3;
-    float v[MAXC][8];
+    float v[MAXC][8], gv[MAXC][8];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
             load8(xr + c * 8, v[j]);
+            load8(g + c * 8, gv[j]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
         }
@@ -111,10 +113,9 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
-            float gv[8], o[8];
-            load8(g + c * 8, gv);
+            float o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[j][i]) * (v[j][i] * rstd);
             store8(yr + c * 8, o);
         }
     }
@@ -151,13 +152,14 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
     const int64_t off = row * width;
     const int64_t slab = rows * width;
     const int nchunk = width >> 3;
-    float v[MAXC][8];
+    float v[MAXC][8], gv[MAXC][8];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
             load8(x + off + c * 8, v[j]);
+            load8(g + c * 8, gv[j]);
             for (int sp = 0; sp < splits; ++sp) {
                 float pv[8];
                 load8(part + sp * slab + off + c * 8, pv);
@@ -174,10 +176,9 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
-            float gv[8], o[8];
-            load8(g + c * 8, gv);
+            float o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[j][i]) * (v[j][i] * rstd);
             store8(y + off + c * 8, o);
         }
     }
