@@ -3,6 +3,8 @@
 A step is one full layer prefill (RMSNorm, QKV projection, QK-norm + RoPE + cache write,
 GQA causal attention, o_proj + residual, RMSNorm, gate/up + SwiGLU, down + residual) of the
 0.6B-shaped layer on one batch of B1 x T2048 synthetic tokens, inputs resident in HBM.
+Each workload first runs untimed for --settle seconds (0.25 by default: the board's clocks and
+power state settle under load), then --warmup untimed steps, then the timed steps.
 Prints ONE JSON line: tokens/s of that step, the roofline fraction of its dominant kernel
 (per-kernel durations from HIP events recorded by the library around each launch, on the
 launch stream), the float64 CPU oracle timed on a bounded sample of the same workload, and,
@@ -64,7 +66,28 @@ def setup_prefill(torch, si, nat, wl, device):
     return layer, w, x, y, kc, vc, ws
 
 
-def time_steps(torch, fn, steps, warmup):
+# Seconds of the same step run before its warmup steps.  The board's clocks and power state take
+# a fraction of a second to settle under load: with the 10 default warmup steps alone (under 2 ms
+# of work) the 0.6B layer's timed steps ran about 8 % slower than after 0.2 s of running.
+SETTLE_S = 0.25
+settle_seconds = SETTLE_S    # set from --settle
+
+
+def settle(torch, fn, seconds):
+    """Run fn until `seconds` of wall time have passed (untimed); returns the number of runs."""
+    t0, n = time.perf_counter(), 0
+    while seconds > 0:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return n
+
+
+def time_steps(torch, fn, steps, warmup, settle_s=None):
+    settle(torch, fn, settle_seconds if settle_s is None else settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -237,9 +260,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 8B prefill, 28-layer stack and 32K decode measurements")
     ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of the 8B prefill / decode runs")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before each workload's warmup steps (clock settling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
     args = ap.parse_args()
+    global settle_seconds
+    settle_seconds = max(0.0, args.settle)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path.", file=sys.stderr)
@@ -273,6 +300,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": settle_seconds,
         "ms_per_step": round(res["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
