@@ -85,6 +85,10 @@ struct RopeTable {
     int T;                   // tokens per sequence
     double turns[64];        // position scale * omega_i / (2 pi)
 };
+// y = bf16(x1 + sum of `splits` fp32 slabs of n elements): the residual add after a split-K
+// down projection
+hipError_t launch_residual_sum_bf16(const float* x1, const float* part, int splits, void* y, int64_t n,
+                                    hipStream_t stream);
 // bf16 input RMSNorm that also writes the RoPE table of its rows
 hipError_t launch_rmsnorm_rope(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
                                float goff, const RopeTable& rope, hipStream_t stream);

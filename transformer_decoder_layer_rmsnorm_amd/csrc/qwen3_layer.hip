@@ -136,7 +136,8 @@ Layout make_layout(const qwen3_config& c, int64_t B, int64_t T, int64_t cap) {
     // split-K partial slabs of o_proj (bf16 prefill with few output tiles)
     int64_t splits = 0;
     if (c.dtype == QWEN3_BF16 && M <= 0x7fffffff) {
-        const int so = gemm_bf16_splits((int)M, (int)H, (int)(Hq * D));
+        const int so = std::max(gemm_bf16_splits((int)M, (int)H, (int)(Hq * D)),
+                                gemm_bf16_splits((int)M, (int)H, (int)I));
         splits = so > 1 ? so : 0;
     }
     L.part_gemm = take(splits * M * H * 4);
@@ -342,9 +343,17 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     }
     STAGE("gemm_gate_up_swiglu", proj(gemm(h2, {L->w.gate_proj, L->w.up_proj}, {I, I}, act, nullptr, M, I, H,
                                            Epilogue::SwiGLU)));
-    // down_proj + residual in the GEMM epilogue (a split here would need a separate reduction pass,
-    // which costs what the split saves)
-    STAGE("gemm_down_residual", proj(gemm(act, {L->w.down_proj}, {H}, y, x1, M, H, I, Epilogue::ResidF32In)));
+    // down_proj + residual: in the GEMM epilogue, or with few output tiles as a split-K GEMM whose
+    // fp32 partial slabs a small pass adds to the residual
+    const int sd = bf ? gemm_bf16_splits(M, H, I) : 1;
+    if (sd > 1) {
+        GemmArgs gd = gemm(act, {L->w.down_proj}, {H}, part, nullptr, M, H, I, Epilogue::PartialF32);
+        gd.splits = sd;
+        STAGE("gemm_down_residual", launch_gemm_bf16(gd, s));
+        STAGE("residual_add", launch_residual_sum_bf16(static_cast<const float*>(x1), part, sd, y, (int64_t)M * H, s));
+    } else {
+        STAGE("gemm_down_residual", proj(gemm(act, {L->w.down_proj}, {H}, y, x1, M, H, I, Epilogue::ResidF32In)));
+    }
 #undef STAGE
     return QWEN3_OK;
 }

@@ -202,6 +202,30 @@ hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, i
     return hipGetLastError();
 }
 
+// y = x1 + sum_s part_s, rounded once to bf16 (the residual add of a split-K down projection):
+// eight elements per thread, the slabs summed in a fixed order.
+__global__ __launch_bounds__(256) void residual_sum_kernel(const float* __restrict__ x1, const float* __restrict__ part,
+                                                           int splits, bf16* __restrict__ y, int64_t n) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    float v[8];
+    load8(x1 + i, v);
+    for (int sp = 0; sp < splits; ++sp) {
+        float pv[8];
+        load8(part + sp * n + i, pv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += pv[e];
+    }
+    store8(y + i, v);
+}
+
+hipError_t launch_residual_sum_bf16(const float* x1, const float* part, int splits, void* y, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if ((n & 7) || splits < 1) return hipErrorInvalidValue;
+    residual_sum_kernel<<<(unsigned)((n / 8 + 255) / 256), 256, 0, s>>>(x1, part, splits, static_cast<bf16*>(y), n);
+    return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(const void* x, DType xt, const void* g, void* y, DType yt, int64_t rows, int width,
                           float eps, float goff, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
