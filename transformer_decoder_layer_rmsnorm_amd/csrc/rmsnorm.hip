@@ -18,7 +18,10 @@
 
 namespace q3 {
 
-template <typename TX, typename TY, int MAXC>
+// EARLY_G: the gains are requested together with the row (a call of a few rows then waits for
+// one memory round trip, not two); for many rows the kernel is bandwidth-bound and the extra
+// registers would only cost occupancy, so the gains are read after the reduction.
+template <typename TX, typename TY, int MAXC, bool EARLY_G>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, const TY* __restrict__ g,
                                                       TY* __restrict__ y, int64_t rows, int width, float eps,
                                                       float goff) {
@@ -30,15 +33,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
     const int nchunk = width >> 3;   // chunks of 8 elements
 
     if (MAXC > 0 && nchunk <= MAXC * kWave) {
-        // the gains are requested with the row, so a few-row call waits for one round trip
-        float v[MAXC][8], gv[MAXC][8];
+        float v[MAXC][8], gv[EARLY_G ? MAXC : 1][8];
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < MAXC; ++j) {
             const int c = lane + j * kWave;
             if (c < nchunk) {
                 load8(xr + c * 8, v[j]);
-                load8(g + c * 8, gv[j]);
+                if constexpr (EARLY_G) load8(g + c * 8, gv[j]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
             }
@@ -49,8 +51,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
             const int c = lane + j * kWave;
             if (c < nchunk) {
                 float o[8];
+                if constexpr (!EARLY_G) load8(g + c * 8, gv[0]);
+                const float* gj = gv[EARLY_G ? j : 0];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[i] = (goff + gv[j][i]) * (v[j][i] * rstd);
+                for (int i = 0; i < 8; ++i) o[i] = (goff + gj[i]) * (v[j][i] * rstd);
                 store8(yr + c * 8, o);
             }
         }
@@ -86,14 +90,13 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
     const bf16* xr = x + row * width;
     bf16* yr = y + row * width;
     const int nchunk = width >> 3;
-    float v[MAXC][8], gv[MAXC][8];
+    float v[MAXC][8];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
             load8(xr + c * 8, v[j]);
-            load8(g + c * 8, gv[j]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
         }
@@ -113,9 +116,10 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
-            float o[8];
+            float gv[8], o[8];
+            load8(g + c * 8, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[j][i]) * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
             store8(yr + c * 8, o);
         }
     }
@@ -134,8 +138,12 @@ template <typename TX, typename TY>
 static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
                                float goff, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
-    rmsnorm_kernel<TX, TY, 8><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
-                                                   static_cast<TY*>(y), rows, width, eps, goff);
+    if (rows <= 1024)   // fewer rows than one per wave slot of the chip: latency-bound
+        rmsnorm_kernel<TX, TY, 8, true><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
+                                                             static_cast<TY*>(y), rows, width, eps, goff);
+    else
+        rmsnorm_kernel<TX, TY, 8, false><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
+                                                              static_cast<TY*>(y), rows, width, eps, goff);
     return hipGetLastError();
 }
 
@@ -152,14 +160,13 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
     const int64_t off = row * width;
     const int64_t slab = rows * width;
     const int nchunk = width >> 3;
-    float v[MAXC][8], gv[MAXC][8];
+    float v[MAXC][8];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
             load8(x + off + c * 8, v[j]);
-            load8(g + c * 8, gv[j]);
             for (int sp = 0; sp < splits; ++sp) {
                 float pv[8];
                 load8(part + sp * slab + off + c * 8, pv);
@@ -176,9 +183,10 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
     for (int j = 0; j < MAXC; ++j) {
         const int c = lane + j * kWave;
         if (c < nchunk) {
-            float o[8];
+            float gv[8], o[8];
+            load8(g + c * 8, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[j][i]) * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
             store8(y + off + c * 8, o);
         }
     }
