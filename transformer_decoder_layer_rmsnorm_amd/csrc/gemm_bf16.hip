@@ -238,13 +238,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(DevGemm p) {
 }
 
 // ------------------------------------------------------------------ QKV projection + QK-norm + RoPE
-// For 128 x 128 tiles, each output tile column block is exactly one head (head_dim 128) of the
-// q | k | v layout, so the epilogue can finish step 3 of the layer in place ("17. A modern
-// architecture: Qwen3", section Attention with grouped KV heads and Q/K normalization: per-head
-// RMSNorm of q and k over head_dim with one gain per projection, then rotate-half RoPE at the
-// token's position; v copied to the cache): the fp32 tile goes to LDS, then 16 lanes per token
-// row normalise, rotate and store it as qhat [B, Hq, T, D] or into the K / V cache slots.  The
-// q / k vectors are normalised from the fp32 accumulators (no bf16 rounding before the norm).
+// Each 128-column block of the q | k | v product is exactly one head (head_dim 128), so the
+// epilogue can finish step 3 of the layer in place ("17. A modern architecture: Qwen3", section
+// Attention with grouped KV heads and Q/K normalization: per-head RMSNorm of q and k over
+// head_dim with one gain per projection, then rotate-half RoPE at the token's position; v copied
+// to the cache): the fp32 tile goes to LDS, then 16 lanes per token row normalise, rotate and
+// store it as qhat [B, Hq, T, D] or into the K / V cache slots.  The q / k vectors are normalised
+// from the fp32 accumulators (no bf16 rounding before the norm); each row's (cos, sin) and cache
+// slot come from the table the input RMSNorm wrote (RopeTable).  128 x 128 register tiles hold
+// one head per tile, 256 x 256 ping-pong tiles two (see gemm_qkv_qkrope_pp_kernel).
 __device__ __forceinline__ float dpp_row_f32(float x, int ctrl_sel) {
     switch (ctrl_sel) {
         case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
