@@ -14,7 +14,8 @@
 // conflicts; each load instruction covers 16 rows of one operand.  Whenever K is a multiple of 64
 // a ping-pong variant of the same tile is used instead: 64-k stages with 128-byte LDS rows (every
 // load moves whole cache lines) and the two wave groups of each SIMD alternating between memory
-// and matrix phases (see gemm_bf16_pp_kernel).
+// and matrix phases (see gemm_bf16_pp_kernel).  The ping-pong kernel also has a 256 x 128 form,
+// used by the fused QKV projection when 256 x 256 tiles would leave too many CUs idle.
 //
 // Smaller tiles (128 x 128 on 4 waves; 64 x 64, or 64 x 128 for SwiGLU, when fewer than 256
 // tiles would remain) keep a register prefetch: BK = 64, two LDS stages, the next k-slab fetched
@@ -558,19 +559,25 @@ __device__ __forceinline__ void vm_wait_at_most(int n) {
     else vm_wait<0>();
 }
 
-constexpr int kPpBM = 256, kPpBN = 256, kPpK = 64;
-constexpr int kPpTM = 64, kPpTN = 128, kPpFM = 2, kPpFN = 4;   // wave tile: 4 x 2 waves
-constexpr int kPpStage = kPpBM * kPpK;                         // elements per operand per stage
+// Tiles are 256 x BN (BN = 256 or 128) over 4 x 2 waves: a wave owns 64 rows and BN / 2 columns.
+constexpr int kPpBM = 256, kPpK = 64;
+constexpr int kPpTM = 64, kPpFM = 2;
+constexpr int kPpStage = kPpBM * kPpK;   // A elements per stage
+template <int BN> struct PpTile {
+    static constexpr int TN = BN / 2, FN = TN / 32;
+    static constexpr int NB = BN / 64;        // B DMA instructions per wave and stage (8 rows each)
+    static constexpr int B_ST = BN * kPpK;    // B elements per stage
+};
 
-// Main loop of the ping-pong kernel: accumulates the workgroup's 256 x 256 tile and hands acc to
+// Main loop of the ping-pong kernel: accumulates the workgroup's 256 x BN tile and hands acc to
 // `epi` with the tile's coordinates.  sA and sB are the kernel's LDS (2 stages each, 1 KB-aligned),
 // free for the epilogue once the loop has ended.
-template <Epilogue EPI, typename Epi>
+template <Epilogue EPI, int BN, typename Epi>
 __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* sB, Epi&& epi) {
-    constexpr int BM = kPpBM, BN = kPpBN, WN = 2, PK = kPpK;
-    constexpr int TM = kPpTM, TN = kPpTN, FM = kPpFM, FN = kPpFN;
+    constexpr int BM = kPpBM, WN = 2, PK = kPpK;
+    constexpr int TM = kPpTM, FM = kPpFM, TN = PpTile<BN>::TN, FN = PpTile<BN>::FN, NB = PpTile<BN>::NB;
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
-    constexpr int A_ST = kPpStage, B_ST = kPpStage;
+    constexpr int A_ST = kPpStage, B_ST = PpTile<BN>::B_ST;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -582,10 +589,10 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
     const int rowbytes = p.K * 2;
 
     // DMA instructions of this wave, 8 tile rows each.  A: two per half h (h = 0: rows
-    // 64 w + 0..31 of every wave row w, h = 1: rows 64 w + 32..63); B: four.  A rows past M read
-    // as zeros (the descriptor covers only the valid rows).
-    int4v ra[2][2], rb[4];
-    int ra_row[2][2], rb_row[4];
+    // 64 w + 0..31 of every wave row w, h = 1: rows 64 w + 32..63); B: BN / 64.  A rows past M
+    // read as zeros (the descriptor covers only the valid rows).
+    int4v ra[2][2], rb[NB];
+    int ra_row[2][2], rb_row[NB];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -598,8 +605,8 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
             ra[h][i] = sgpr_desc(p.a + (int64_t)min(r0, p.M - 1) * p.K, nrows * rowbytes);
         }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int lr = (wave * 4 + i) * 8;
+    for (int i = 0; i < NB; ++i) {
+        const int lr = (wave * NB + i) * 8;
         rb_row[i] = lr;
         const bf16* base;
         if constexpr (DUAL) {
@@ -619,11 +626,11 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
     const int voff_odd = r8 * rowbytes + (((lane & 7) ^ swz8(8 + r8)) << 4);
     const unsigned sA_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sA;
     const unsigned sB_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sB;
-    auto issue_b_a0 = [&](int st) {   // 6 loads
+    auto issue_b_a0 = [&](int st) {   // NB + 2 loads
         const int slot = st & 1;
         const int soff = st * (PK * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NB; ++i)
             dma16(rb[i], ((rb_row[i] >> 3) & 1) ? voff_odd : voff_even, soff,
                   __builtin_amdgcn_readfirstlane(sB_lds + (slot * B_ST + rb_row[i] * PK) * 2));
 #pragma unroll
@@ -665,7 +672,7 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
     issue_b_a0(0);
     issue_a1(0);
     if (nst > 1) issue_b_a0(1);
-    vm_wait_at_most(nst > 1 ? 8 : 2);
+    vm_wait_at_most(nst > 1 ? NB + 4 : 2);
     barrier_only();
     if (grp == 1) barrier_only();
     bf16x8 af[4], bfr[4][FN];
@@ -686,10 +693,10 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
             for (int q = 0; q < 4; ++q) af[q] = *reinterpret_cast<const bf16x8*>(pa + a_rd[q] + i * 32 * PK);
             if (i == 0) {
                 if (t + 1 < nst) issue_a1(t + 1);
-                vm_wait_at_most(t + 1 < nst ? 8 : 0);
+                vm_wait_at_most(t + 1 < nst ? NB + 4 : 0);
             } else {
                 if (t + 2 < nst) issue_b_a0(t + 2);
-                vm_wait_at_most((t + 1 < nst ? 2 : 0) + (t + 2 < nst ? 6 : 0));
+                vm_wait_at_most((t + 1 < nst ? 2 : 0) + (t + 2 < nst ? NB + 2 : 0));
             }
             lgkm_wait0();
             barrier_only();
@@ -708,47 +715,52 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
     epi(acc, m0, tn, wm, wn, lane);
 }
 
-template <Epilogue EPI>
+template <Epilogue EPI, int BN>
 __global__ __launch_bounds__(512) void gemm_bf16_pp_kernel(DevGemm p) {
+    using T = PpTile<BN>;
     __shared__ __attribute__((aligned(1024))) bf16 sA[2 * kPpStage];
-    __shared__ __attribute__((aligned(1024))) bf16 sB[2 * kPpStage];
-    gemm_pp_body<EPI>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][kPpFN], int m0, int tn, int wm, int wn, int lane) {
-        write_tile<EPI, kPpBN, kPpTM, kPpTN, kPpFM, kPpFN>(p, acc, m0, tn, wm, wn, lane);
+    __shared__ __attribute__((aligned(1024))) bf16 sB[2 * T::B_ST];
+    gemm_pp_body<EPI, BN>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][T::FN], int m0, int tn, int wm, int wn, int lane) {
+        write_tile<EPI, BN, kPpTM, T::TN, kPpFM, T::FN>(p, acc, m0, tn, wm, wn, lane);
     });
 }
 
-// QKV projection on 256 x 256 ping-pong tiles with the QK-norm + RoPE + cache write epilogue
-// (same per-row work as gemm_qkv_qkrope_kernel).  A tile spans two heads, one per wave column
-// (wn), so the epilogue runs twice: the waves of column h put their fp32 accumulators for head
-// 2 tn + h into LDS (256 rows x 136 floats, over the stage buffers), then all 512 threads
-// finish its 256 token rows.
+// QKV projection on 256 x BN ping-pong tiles with the QK-norm + RoPE + cache write epilogue
+// (same per-row work as gemm_qkv_qkrope_kernel).  A tile spans BN / 128 heads; per head, the
+// waves whose columns lie in it put their fp32 accumulators into LDS (256 rows x 136 floats,
+// over the stage buffers), then all 512 threads finish its 256 token rows.  With BN = 256 each
+// wave column is one head (two passes), with BN = 128 the two wave columns are its halves.
 constexpr int kPpQkTP = 128 + 8;
+template <int BN>
 __global__ __launch_bounds__(512) void gemm_qkv_qkrope_pp_kernel(DevGemm p, QkPpArgs a) {
-    constexpr int TP = kPpQkTP;
-    constexpr int SMEM = (kPpBM * TP * 4 > 4 * kPpStage * 2) ? kPpBM * TP * 4 : 4 * kPpStage * 2;
+    using T = PpTile<BN>;
+    constexpr int TP = kPpQkTP, HPT = BN / 128;
+    constexpr int LOOP = 2 * (kPpStage + T::B_ST) * 2;
+    constexpr int SMEM = (kPpBM * TP * 4 > LOOP) ? kPpBM * TP * 4 : LOOP;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
     bf16* sA = reinterpret_cast<bf16*>(smem);
     bf16* sB = sA + 2 * kPpStage;
-    gemm_pp_body<Epilogue::Store>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][kPpFN], int m0, int tn, int wm, int wn,
-                                                 int lane) {
+    gemm_pp_body<Epilogue::Store, BN>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][T::FN], int m0, int tn, int wm,
+                                                     int wn, int lane) {
         float* tile = reinterpret_cast<float*>(smem);
         const int jl = threadIdx.x & 15;
+        const int wh = (wn * T::TN) / 128, wc = (wn * T::TN) % 128;   // the wave's head and column in it
         __syncthreads();   // every wave is past its last LDS fragment read
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            if (wn == hh) {
+        for (int hh = 0; hh < HPT; ++hh) {
+            if (wh == hh) {
 #pragma unroll
                 for (int i = 0; i < kPpFM; ++i)
 #pragma unroll
-                    for (int j = 0; j < kPpFN; ++j)
+                    for (int j = 0; j < T::FN; ++j)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int row = wm * kPpTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                            tile[row * TP + j * 32 + (lane & 31)] = acc[i][j][r];
+                            tile[row * TP + wc + j * 32 + (lane & 31)] = acc[i][j][r];
                         }
             }
             __syncthreads();
-            const int hs = 2 * tn + hh;
+            const int hs = HPT * tn + hh;
             float g[8];
             qkrope_gains(a, hs, jl, g);
 #pragma unroll 1
@@ -899,13 +911,13 @@ static hipError_t run_dma_tile(DevGemm p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <Epilogue EPI>
+template <Epilogue EPI, int BN = 256>
 static hipError_t run_pp_tile(DevGemm p, hipStream_t s) {
-    const int bn_out = (EPI == Epilogue::SwiGLU) ? 128 : 256;
+    const int bn_out = (EPI == Epilogue::SwiGLU) ? BN / 2 : BN;
     if (p.N % bn_out || p.K % 64 || (int64_t)p.K * 2 * 8 >= (int64_t)1 << 31) return hipErrorInvalidValue;
     p.tiles_m = (p.M + 255) / 256;
     p.tiles_n = p.N / bn_out;
-    gemm_bf16_pp_kernel<EPI><<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p);
+    gemm_bf16_pp_kernel<EPI, BN><<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -940,9 +952,12 @@ static int qkv_fused_kind(const GemmArgs& g, const QkRopeArgs& a) {
     if (!a.rope_cs || !a.rope_slot || g.M != a.B * a.T) return 0;
     if (g.N != (a.Hq + 2 * a.Hkv) * 128 || g.K % BK || g.K % kPpK) return 0;
     const long tiles256 = (long)((g.M + 255) / 256) * (g.N / 256);
+    const long tiles_pp128 = (long)((g.M + 255) / 256) * (g.N / 128);
     const long tiles128 = (long)((g.M + 127) / 128) * (g.N / 128);
-    if (tiles256 >= 192 && g.N % 256 == 0) return (int64_t)g.K * 2 * 8 < ((int64_t)1 << 31) ? 2 : 0;
+    const bool dma_ok = (int64_t)g.K * 2 * 8 < ((int64_t)1 << 31);
+    if (tiles256 >= 192 && g.N % 256 == 0) return dma_ok ? 2 : 0;
     if (tiles256 >= 256 && g.N % 256 == 0) return 0;
+    if (tiles_pp128 >= 256 && dma_ok) return 3;
     return tiles128 >= 256 ? 1 : 0;
 }
 
@@ -955,10 +970,16 @@ hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStr
     p.splits = 1;
     if (kind == 2) {
         p.tiles_m = (p.M + kPpBM - 1) / kPpBM;
-        p.tiles_n = p.N / kPpBN;
+        p.tiles_n = p.N / 256;
         const QkPpArgs pa{a.q_norm, a.k_norm, a.qhat, a.k_cache, a.v_cache, a.rope_cs, a.rope_slot,
                           a.T, a.Hq, a.Hkv, a.cap, a.eps, a.goff};
-        gemm_qkv_qkrope_pp_kernel<<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p, pa);
+        gemm_qkv_qkrope_pp_kernel<256><<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p, pa);
+    } else if (kind == 3) {
+        p.tiles_m = (p.M + kPpBM - 1) / kPpBM;
+        p.tiles_n = p.N / 128;
+        const QkPpArgs pa{a.q_norm, a.k_norm, a.qhat, a.k_cache, a.v_cache, a.rope_cs, a.rope_slot,
+                          a.T, a.Hq, a.Hkv, a.cap, a.eps, a.goff};
+        gemm_qkv_qkrope_pp_kernel<128><<<(unsigned)(p.tiles_m * p.tiles_n), 512, 0, s>>>(p, pa);
     } else {
         p.tiles_m = (p.M + 127) / 128;
         p.tiles_n = p.N / 128;
