@@ -301,6 +301,27 @@ struct QkPpArgs {
     float eps, goff;
 };
 
+// A token row's entries of the RoPE table for lane jl: (cos, sin) of frequencies 4jl..4jl+3
+// and the row's cache slot.  The epilogues fetch them for all their rows before the tile goes
+// through LDS, so the table's latency overlaps that step instead of every row's processing.
+struct RopeRow {
+    f32x4 c01, c23;
+    int lin;
+};
+template <typename Args>
+__device__ __forceinline__ RopeRow rope_row_load(int m, int jl, bool need_cs, bool need_slot, const DevGemm& p,
+                                                 const Args& a) {
+    const int mc = m < p.M ? m : p.M - 1;
+    RopeRow r{};
+    if (need_cs) {
+        const float* csr = a.rope_cs + (int64_t)mc * 128 + 8 * jl;
+        r.c01 = *reinterpret_cast<const f32x4*>(csr);
+        r.c23 = *reinterpret_cast<const f32x4*>(csr + 4);
+    }
+    if (need_slot) r.lin = a.rope_slot[mc];
+    return r;
+}
+
 // Token row m of head hs (q, k or v column block of the QKV product), fp32 values at `tr`:
 // q and k are RMS-normalised over the head, scaled by their gains and rotated with the row's
 // (cos, sin) from the RoPE table, then stored to qhat or the K cache slot; v is rounded and
@@ -309,7 +330,7 @@ struct QkPpArgs {
 // the reduction even when m >= M (its loads are clamped and its store is skipped).
 template <typename Args>
 __device__ __forceinline__ void qkrope_row(const float* tr, int jl, int m, int hs, const float (&g)[8],
-                                           const DevGemm& p, const Args& a) {
+                                           const DevGemm& p, const Args& a, const RopeRow& rr) {
     constexpr int D = 128;
     // the argument's fields as values (selecting between fields would index the argument)
     void* qhat = a.qhat;
@@ -321,7 +342,7 @@ __device__ __forceinline__ void qkrope_row(const float* tr, int jl, int m, int h
     const bool valid = m < p.M;
     const int mc = valid ? m : p.M - 1;
     const int b = mc / a.T, t = mc - b * a.T;
-    const int lin = a.rope_slot[mc];
+    const int lin = rr.lin;
     const f32x4 lo = *reinterpret_cast<const f32x4*>(tr + 4 * jl);
     const f32x4 hi = *reinterpret_cast<const f32x4*>(tr + 64 + 4 * jl);
     bf16x4 olo, ohi;
@@ -331,9 +352,7 @@ __device__ __forceinline__ void qkrope_row(const float* tr, int jl, int m, int h
         for (int e = 0; e < 4; ++e) { olo[e] = (bf16)lo[e]; ohi[e] = (bf16)hi[e]; }
         dst = static_cast<bf16*>(vc) + (((int64_t)b * Hkv + (hs - Hq - Hkv)) * a.cap + lin) * D;
     } else {
-        const float* csr = a.rope_cs + (int64_t)mc * 128 + 8 * jl;   // (cos, sin) of 4jl..4jl+3
-        const f32x4 c01 = *reinterpret_cast<const f32x4*>(csr);
-        const f32x4 c23 = *reinterpret_cast<const f32x4*>(csr + 4);
+        const f32x4 c01 = rr.c01, c23 = rr.c23;   // (cos, sin) of 4jl..4jl+3
         const float cs[4] = {c01[0], c01[2], c23[0], c23[2]}, sn[4] = {c01[1], c01[3], c23[1], c23[3]};
         float ss = 0.f;
 #pragma unroll
@@ -362,6 +381,12 @@ __global__ __launch_bounds__(256) void gemm_qkv_qkrope_kernel(DevGemm p, QkRopeA
     gemm_bf16_body<Epilogue::Store, BM, BN, WM, WN>(p, smem, [&](const f32x16 (&acc)[FM][FN], int m0, int tn,
                                                                  int wm, int wn, int lane, int) {
         float* tile = reinterpret_cast<float*>(smem);
+        const int jl = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+        constexpr int NR = BM / 16;   // token rows per thread
+        const bool need_cs = tn < a.Hq + a.Hkv, need_slot = tn >= a.Hq;   // q/k rotate, k/v go to the cache
+        RopeRow rr[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) rr[k] = rope_row_load(m0 + r0 + 16 * k, jl, need_cs, need_slot, p, a);
         // the main loop ended with a barrier: every wave is done reading its last k-slab
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -373,10 +398,13 @@ __global__ __launch_bounds__(256) void gemm_qkv_qkrope_kernel(DevGemm p, QkRopeA
                     tile[row * TP + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
                 }
         __syncthreads();
-        const int jl = threadIdx.x & 15;
         float g[8];
         qkrope_gains(a, tn, jl, g);   // the column block is head tn of the q | k | v layout
-        for (int row = threadIdx.x >> 4; row < BM; row += 16) qkrope_row(tile + row * TP, jl, m0 + row, tn, g, p, a);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int row = r0 + 16 * k;
+            qkrope_row(tile + row * TP, jl, m0 + row, tn, g, p, a, rr[k]);
+        }
     });
 }
 
@@ -743,8 +771,18 @@ __global__ __launch_bounds__(512) void gemm_qkv_qkrope_pp_kernel(DevGemm p, QkPp
     gemm_pp_body<Epilogue::Store, BN>(p, sA, sB, [&](const f32x16 (&acc)[kPpFM][T::FN], int m0, int tn, int wm,
                                                      int wn, int lane) {
         float* tile = reinterpret_cast<float*>(smem);
-        const int jl = threadIdx.x & 15;
+        const int jl = threadIdx.x & 15, r0 = threadIdx.x >> 4;
         const int wh = (wn * T::TN) / 128, wc = (wn * T::TN) % 128;   // the wave's head and column in it
+        constexpr int NR = kPpBM / 32;   // token rows per thread
+        // the table entries serve every head of the tile: q and k heads rotate, k and v heads
+        // go to the cache
+        int Hq = a.Hq, Hkv = a.Hkv;
+        asm("" : "+s"(Hq), "+s"(Hkv));
+        const int h0 = HPT * tn, h1 = HPT * tn + HPT - 1;
+        const bool need_cs = h0 < Hq + Hkv, need_slot = h1 >= Hq;
+        RopeRow rr[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) rr[k] = rope_row_load(m0 + r0 + 32 * k, jl, need_cs, need_slot, p, a);
         __syncthreads();   // every wave is past its last LDS fragment read
 #pragma unroll
         for (int hh = 0; hh < HPT; ++hh) {
@@ -763,8 +801,11 @@ __global__ __launch_bounds__(512) void gemm_qkv_qkrope_pp_kernel(DevGemm p, QkPp
             const int hs = HPT * tn + hh;
             float g[8];
             qkrope_gains(a, hs, jl, g);
-#pragma unroll 1
-            for (int row = threadIdx.x >> 4; row < kPpBM; row += 32) qkrope_row(tile + row * TP, jl, m0 + row, hs, g, p, a);
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const int row = r0 + 32 * k;
+                qkrope_row(tile + row * TP, jl, m0 + row, hs, g, p, a, rr[k]);
+            }
             __syncthreads();   // the tile is rewritten by the next head's waves
         }
     });
