@@ -66,6 +66,17 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
+// v of lane l and of lane l ^ 32, in (a, b): v_permlane32_swap exchanges the upper 32 lanes of its
+// first operand with the lower 32 lanes of its second, so with v in both each lane holds both
+// values afterwards, at VALU latency (a ds_bpermute would be an LDS round trip).  Written as
+// assembly because the compiler folds the builtin's two results into one when both operands
+// hold the same value; the s_nop covers the VALU-write-to-permlane-read hazard.
+__device__ __forceinline__ void pair_xor32(float v, float& a, float& b) {
+    a = v;
+    b = v;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
     return __builtin_bit_cast(bf16x4, r);
@@ -238,7 +249,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
         for (int i = 0; i < NKB; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[i][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
+        {
+            float m0v, m1v;
+            pair_xor32(mt, m0v, m1v);
+            mt = fmaxf(m0v, m1v) * sl2;
+        }
         if (__any(mt > m_run + 8.f)) {
             const float m_new = fmaxf(m_run, mt);
             const float corr = fast_exp2(m_run - m_new);
@@ -336,7 +351,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     }
 
     // normalise and store: lane holds d = db*32 + 8(r/4) + 4(lane/32) + r%4 of its query
-    const float inv = 1.0f / (l_run + __shfl_xor(l_run, 32, 64));
+    float l0v, l1v;
+    pair_xor32(l_run, l0v, l1v);
+    const float inv = 1.0f / (l0v + l1v);
     const int q = qw + (lane & 31);
     if (q < a.T) {
         bf16* orow = static_cast<bf16*>(a.out) + ((int64_t)b * a.T + q) * a.Hq * HD + (int64_t)h * HD;
