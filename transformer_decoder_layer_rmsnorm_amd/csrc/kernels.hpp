@@ -146,9 +146,9 @@ struct QkRopeArgs {
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
 // QKV projection with QK-norm + RoPE + cache write fused into its epilogue (bf16, head_dim 128,
-// full split-half RoPE, prefill shapes that take 128 x 128 register tiles or, with positions
-// that are zero or in device arrays, 256 x 256 ping-pong tiles); `fusable` says whether the
-// combination applies, else the caller runs the GEMM and launch_qknorm_rope separately.
+// full split-half RoPE over the head, prefill shapes on 256 x 256 or 256 x 128 ping-pong tiles or
+// 128 x 128 register tiles, rope_cs / rope_slot set); `fusable` says whether the combination
+// applies, else the caller runs the GEMM and launch_qknorm_rope separately.
 bool gemm_qkv_fusable(const GemmArgs& g, const QkRopeArgs& a);
 hipError_t launch_gemm_qkv_qkrope(const GemmArgs& g, const QkRopeArgs& a, hipStream_t stream);
 

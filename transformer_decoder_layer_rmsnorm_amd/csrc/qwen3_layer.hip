@@ -270,7 +270,7 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     qa.goff = gain_off;
     qa.rotary_dim = c.rotary_dim;
     qa.adjacent = c.rope_adjacent_pairs;
-    // QKV projection; for prefill shapes (256 x 256 ping-pong or 128 x 128 register tiles) the
+    // QKV projection; for prefill shapes (256 x 256 or 256 x 128 ping-pong tiles, else 128 x 128) the
     // QK-norm + RoPE + cache write runs in the GEMM's epilogue (one kernel), otherwise as its own
     // kernel.  The fused epilogue reads each row's RoPE angles and cache slot from a table that
     // the input RMSNorm writes into the x1 and h2 regions, which are free until o_proj.
