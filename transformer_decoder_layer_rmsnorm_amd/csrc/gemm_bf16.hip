@@ -15,10 +15,12 @@
 // a ping-pong variant of the same tile is used instead: 64-k stages with 128-byte LDS rows (every
 // load moves whole cache lines) and the two wave groups of each SIMD alternating between memory
 // and matrix phases (see gemm_bf16_pp_kernel).  The ping-pong kernel also has a 256 x 128 form,
-// used by the fused QKV projection when 256 x 256 tiles would leave too many CUs idle.
+// used by the fused QKV projection when 256 x 256 tiles would leave too many CUs idle.  Its
+// epilogues that read a residual stage the tile through LDS and move 16 bytes per lane (see
+// pp_store_tile).
 //
 // Smaller tiles (128 x 128 on 4 waves; 64 x 64, or 64 x 128 for SwiGLU, when fewer than 256
-// tiles would remain) keep a register prefetch: BK = 64, two LDS stages, the next k-slab fetched
+// tiles would remain; 64 x 128 for split-K partial slabs) keep a register prefetch: BK = 64, two LDS stages, the next k-slab fetched
 // into registers while the current one feeds the MFMAs, two or more workgroups per CU.  Their LDS
 // rows are padded to 144 bytes: the 16 lanes served per cycle by the 64-bank LDS then read 16 rows
 // of the same 16-byte chunk from 16 disjoint bank groups.
@@ -1074,9 +1076,10 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
         return run_tile<EPI, 64, 64, 2, 2>(p, s);
 }
 
-// Which fused QKV kernel serves the projection g (0: none): the tiles the generic launcher would
-// pick, 256 x 256 ping-pong (2) or 128 x 128 register tiles (1), provided each head is a whole
-// 128-column block and the RoPE is the plain rotate-half over the full head.
+// Which fused QKV kernel serves the projection g (0: none): 256 x 256 ping-pong tiles (2) when the
+// generic launcher would take them, else 256 x 128 ping-pong tiles (3) when those give a
+// workgroup per CU, else 128 x 128 register tiles (1); provided each head is a whole 128-column
+// block and the RoPE is the plain rotate-half over the full head.
 static int qkv_fused_kind(const GemmArgs& g, const QkRopeArgs& a) {
     if (g.epi != Epilogue::Store || g.M <= 64 || a.D != 128 || a.rotary_dim != 128 || a.adjacent || a.local.rolling)
         return 0;
