@@ -160,32 +160,41 @@ def test_bf16_padded_many_sequences_ping_pong_qkv_epilogue():
     _check_cache(to_np(kd), to_np(vd), knew, vnew, starts, t, "padded prefill (ping-pong epilogue)")
 
 
-def test_bf16_padded_prefix_0p6b_fused_qkv_epilogue():
-    # 0.6B shapes, 2 sequences x 1024 tokens after prefixes of 100 and 37 keys, the second with
-    # 300 tokens of left padding: the QKV projection (2048 x 4096) takes the 128 x 128 kernel with
-    # the QK-norm / RoPE / cache-write epilogue, whose angles and slots come from the table the
-    # input RMSNorm builds from the inline starts and padding
+def _padded_prefix_0p6b(b, t, starts, pads, seed, what):
     wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
     cfg = wl.cfg
-    gl = GpuLayer.seeded(cfg, seed=39)
-    b, t = 2, 1024
-    starts, pads = [100, 37], [0, 300]
+    gl = GpuLayer.seeded(cfg, seed=seed)
     hkv, d = cfg.num_key_value_heads, cfg.head_dim
     cap = max(starts) + t
-    log(f"bf16 padded prefill on prefixes, 0.6B shapes, B{b} T{t} (128 x 128 fused QKV epilogue)")
+    log(f"bf16 padded prefill on prefixes, 0.6B shapes, B{b} T{t} ({what})")
     kc = np.zeros((b, hkv, cap, d), np.float32)
     vc = np.zeros((b, hkv, cap, d), np.float32)
     for i, n in enumerate(starts):
         for h in range(hkv):
-            kc[i, h, :n] = si.cache_block(cfg, "k", i, h, n, seed=39)
-            vc[i, h, :n] = si.cache_block(cfg, "v", i, h, n, seed=39)
+            kc[i, h, :n] = si.cache_block(cfg, "k", i, h, n, seed=seed)
+            vc[i, h, :n] = si.cache_block(cfg, "v", i, h, n, seed=seed)
     kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
     kc16, vc16 = to_np(kd), to_np(vd)
-    x = si.layer_input(cfg, b, t, seed=39)
+    x = si.layer_input(cfg, b, t, seed=seed)
     y, kd, vd, _ = gl.prefill(to_dev(x, cfg), cap=cap, caches=(kd, vd), starts=starts, pads=pads)
     ref, knew, vnew = oracle.layer_prefill_padded(x, gl.w_np, cfg, kc16, vc16, starts, pads)
-    assert_bf16_parity(to_np(y), ref, "padded prefill y on prefixes (0.6B shapes)")
-    _check_cache(to_np(kd), to_np(vd), knew, vnew, starts, t, "padded prefill (fused 128 x 128 epilogue)")
+    assert_bf16_parity(to_np(y), ref, f"padded prefill y on prefixes (0.6B shapes, {what})")
+    _check_cache(to_np(kd), to_np(vd), knew, vnew, starts, t, f"padded prefill ({what})")
+
+
+def test_bf16_padded_prefix_0p6b_fused_qkv_epilogue():
+    # 0.6B shapes, 2 sequences x 1024 tokens after prefixes of 100 and 37 keys, the second with
+    # 300 tokens of left padding: the QKV projection (2048 x 4096) takes 256 x 128 ping-pong
+    # tiles with the QK-norm / RoPE / cache-write epilogue, whose angles and slots come from the
+    # table the input RMSNorm builds from the inline starts and padding
+    _padded_prefix_0p6b(2, 1024, [100, 37], [0, 300], 39, "fused 256 x 128 ping-pong epilogue")
+
+
+def test_bf16_padded_prefix_0p6b_fused_qkv_register_tiles():
+    # one sequence of 1200 tokens after a 100-key prefix, 300 of them left padding: the QKV
+    # projection (1200 x 4096) has too few 256-row tiles for the ping-pong forms and takes the
+    # 128 x 128 register-tile kernel with the same epilogue, its last row tile partial (48 rows)
+    _padded_prefix_0p6b(1, 1200, [100], [300], 40, "fused 128 x 128 epilogue")
 
 
 def test_f32_padded_prefill_and_decode():

@@ -68,9 +68,9 @@ def test_qwen3_8b_layer_prefill_ragged_tail_rows():
 
 
 def test_qwen3_0p6b_layer_prefill_ragged_tail_rows():
-    """0.6B shapes at T = 2088 (32 whole 64-row tiles plus a 40-row tail): down_proj takes the
-    64 x 64 register tiles, gate/up the ping-pong tiles, QKV the fused 128 x 128 kernel and
-    o_proj the split-K tiles, all with a partial last row tile; rows in and around the tail are
+    """0.6B shapes at T = 2088 (32 whole 64-row tiles plus a 40-row tail): o_proj and down take
+    the split-K 64 x 128 tiles, gate/up the 256 x 256 ping-pong tiles, QKV the fused 256 x 128
+    ping-pong kernel, all with a partial last row tile; rows in and around the tail are
     checked."""
     wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
     cfg = wl.cfg
