@@ -61,8 +61,12 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // silu(g) * u in fp32 (silu(z) = z * sigmoid(z)).
+// SiLU(g) * u = g * u / (1 + e^-g).  The reciprocal is the hardware's v_rcp_f32 (about 1 ulp):
+// an IEEE-exact division expands to about ten instructions per element, which the SwiGLU
+// epilogues pay with the matrix cores idle, and the result is rounded to bf16 (or compared at
+// 1e-4 in fp32) anyway.  g -> -inf gives NaN either way; a finite g far below zero gives -0.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 }  // namespace q3
