@@ -1,22 +1,33 @@
 """Benchmark of the Qwen3-style decoder layer on one MI355X.
 
-A step is one full layer prefill (RMSNorm, QKV projection, QK-norm + RoPE + cache write,
-GQA causal attention, o_proj + residual, RMSNorm, gate/up + SwiGLU, down + residual) of the
-0.6B-shaped layer on one batch of B1 x T2048 synthetic tokens, inputs resident in HBM.
-Each workload first runs untimed for --settle seconds (0.25 by default: the board's clocks and
-power state settle under load), then --warmup untimed steps, then the timed steps.
-Prints ONE JSON line: tokens/s of that step, the roofline fraction of its dominant kernel
-(per-kernel durations from HIP events recorded by the library around each launch, on the
-launch stream), the float64 CPU oracle timed on a bounded sample of the same workload, and,
-as extra context, the 8B-shaped layer prefill (B1 T8192), the 28-layer 0.6B-shaped stack with its
-final norm (B4 T4096) and the 8B-shaped decode step on a 32768-key cache (decode attention
-achieved GB/s against HBM peak).
+A step is one full layer prefill (RMSNorm, QKV projection, QK-norm + RoPE + cache write, GQA
+causal attention, o_proj + residual, RMSNorm, gate/up + SwiGLU, down + residual) of the
+8B-shaped layer (hidden 4096, 32 / 8 heads of 128, intermediate 12288) on one batch of B1 x T8192
+synthetic tokens, inputs resident in HBM: the largest of the workloads that fits one GPU.
+
+Each workload first runs untimed for --settle seconds (the board's clocks and power state
+settle under load), then --warmup untimed steps, then the timed steps between two HIP events on
+the launch stream (the mean), then as many again with an event between consecutive steps (the
+median).  A further untimed pass with the library's per-launch events gives the per-kernel
+durations from which the roofline fraction of the dominant kernel is taken.
+
+Prints ONE JSON line: tokens/s of the headline step and the roofline of its dominant kernel;
+under "workloads" the same record for the 0.6B-shaped layer prefill (B1 T2048), the 28-layer
+0.6B-shaped stack with its final norm (B4 T4096), the 8B-shaped decode step on a 32768-key cache
+(B16; decode attention and whole-layer bytes against HBM peak) and the tiny fp32 layer; and the
+float64 CPU oracle timed on bounded samples of the same workloads, with the parity of the GPU
+result against it on identical inputs.
+
+`--summarize-rocprof DB` (no GPU needed) prints a markdown summary of a rocprofv3 database of
+this benchmark: per-kernel durations, or FETCH_SIZE / WRITE_SIZE, or MFMA utilisation and clock.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -25,7 +36,19 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 METRIC = "Qwen3-layer prefill tokens/s & % MFMA peak; 32K decode attn % HBM BW"
+CU_COUNT = 256
 
+SHORT = {"c1": "tiny-f32-layer", "c2": "qwen3-0.6b-layer-prefill", "c3": "qwen3-0.6b-stack28-prefill",
+         "c4": "qwen3-8b-layer-prefill", "c5": "qwen3-8b-layer-decode-32k"}
+HEADLINE = "qwen3-8b-layer-prefill"
+
+# parity bars: fp32 max-abs; bf16 mean relative error and max-abs scaled by the output RMS
+F32_MAX_ABS = 1e-4
+BF16_MEAN_REL = 5e-3
+BF16_MAX_ABS = 3e-2
+
+
+# ------------------------------------------------------------------------------ work counts
 
 def layer_flops(cfg, b, t):
     """Algorithmic FLOPs per launch of each prefill stage (2*M*N*K for projections; causal
@@ -48,186 +71,101 @@ def decode_attention_bytes(cfg, b, cached):
     return 2.0 * b * cfg.num_key_value_heads * (cached + 1) * cfg.head_dim * 2
 
 
-def setup_prefill(torch, si, nat, wl, device):
-    cfg = wl.cfg
-    g = torch.Generator(device=device).manual_seed(wl.seed)
-    dt = torch.bfloat16
-    w = {}
-    for name, shape in si.weight_shapes(cfg).items():
-        z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-        w[name] = ((1 + 0.1 * z) if name in si.GAIN_NAMES else 0.02 * z).to(dt)
-    layer = nat.Layer(cfg, w)
-    x = torch.randn((wl.batch, wl.seq_len, cfg.hidden_size), generator=g, device=device).to(dt)
-    y = torch.empty_like(x)
-    cap = wl.seq_len + wl.cached
-    kc = torch.zeros((wl.batch, cfg.num_key_value_heads, cap, cfg.head_dim), dtype=dt, device=device)
-    vc = torch.zeros_like(kc)
-    ws = torch.empty(layer.workspace_size(wl.batch, wl.seq_len, cap), dtype=torch.uint8, device=device)
-    return layer, w, x, y, kc, vc, ws
+def decode_weight_bytes(cfg):
+    """bf16 weight bytes one decode step streams: q, k, v, o, gate, up, down (+ the gains)."""
+    h, d, hq, hkv, i = cfg.hidden_size, cfg.head_dim, cfg.num_attention_heads, cfg.num_key_value_heads, \
+        cfg.intermediate_size
+    return 2.0 * (h * (hq + 2 * hkv) * d + hq * d * h + 3 * h * i + 2 * h + 2 * d)
 
 
-# Seconds of the same step run before its warmup steps.  The board's clocks and power state take
-# a fraction of a second to settle under load: with the 10 default warmup steps alone (under 2 ms
-# of work) the 0.6B layer's timed steps ran about 8 % slower than after 0.2 s of running.
-SETTLE_S = 0.25
-settle_seconds = SETTLE_S    # set from --settle
-
-
-def settle(torch, fn, seconds):
-    """Run fn until `seconds` of wall time have passed (untimed); returns the number of runs."""
-    t0, n = time.perf_counter(), 0
-    while seconds > 0:
-        for _ in range(8):
-            fn()
-        torch.cuda.synchronize()
-        n += 8
-        if time.perf_counter() - t0 >= seconds:
-            break
-    return n
-
-
-def time_steps(torch, fn, steps, warmup, settle_s=None):
-    settle(torch, fn, settle_seconds if settle_s is None else settle_s)
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        fn()
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
-
-
-def profile_steps(torch, layer, fn, steps):
-    layer.set_profiling(True)
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    prof = layer.read_profile()
-    layer.set_profiling(False)
-    return {k: v[1] / v[0] for k, v in prof.items()}     # average ms per launch
+def decode_skinny_bytes(cfg):
+    """Weight bytes of each skinny projection stage of a decode step."""
+    h, d, hq, hkv, i = cfg.hidden_size, cfg.head_dim, cfg.num_attention_heads, cfg.num_key_value_heads, \
+        cfg.intermediate_size
+    return {"gemm_qkv": 2.0 * h * (hq + 2 * hkv) * d, "gemm_o_residual": 2.0 * hq * d * h,
+            "gemm_gate_up_swiglu": 4.0 * h * i, "gemm_down_residual": 2.0 * h * i}
 
 
 # stages that run a GEMM of the table above with more work fused into its epilogue
 FUSED_ALIASES = {"gemm_qkv_qknorm_rope": "gemm_qkv"}
 
 
-def stage_flops(flops, stage):
-    return flops.get(stage, flops.get(FUSED_ALIASES.get(stage, ""), None))
+def stage_work(work, stage):
+    return work.get(stage, work.get(FUSED_ALIASES.get(stage, ""), None))
 
 
-def kernel_table(avg_ms, flops):
+# ------------------------------------------------------------------------------ timing
+
+SETTLE_S = 0.25
+settle_seconds = SETTLE_S    # set from --settle
+
+
+def settle(torch, fn, seconds):
+    """Run fn until `seconds` of wall time have passed (untimed)."""
+    t0 = time.perf_counter()
+    while seconds > 0:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+
+
+def time_steps(torch, fn, steps, warmup):
+    """ms per step over exactly `steps` timed steps between two events on the launch stream
+    (synchronised before and after), and the median step from a second run of `steps` with an
+    event between consecutive steps."""
+    settle(torch, fn, settle_seconds)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    mean = t0.elapsed_time(t1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return mean, statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+
+
+def profile_steps(torch, layers, fn, steps):
+    """Average ms per launch of every stage, from the library's events around each launch."""
+    for layer in layers:
+        layer.set_profiling(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    tot = {}
+    for layer in layers:
+        for k, (n, ms) in layer.read_profile().items():
+            c = tot.setdefault(k, [0, 0.0])
+            c[0] += n
+            c[1] += ms
+        layer.set_profiling(False)
+    return {k: v[1] / v[0] for k, v in tot.items()}
+
+
+def kernel_table(avg_ms, flops=None, byts=None):
     out = {}
     for k, ms in avg_ms.items():
         e = {"avg_ms": round(ms, 5)}
-        f = stage_flops(flops, k)
+        f = stage_work(flops, k) if flops else None
         if f is not None:
             tf = f / (ms * 1e-3) / 1e12
             e.update(tflops=round(tf, 1), frac_of_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        b = stage_work(byts, k) if byts else None
+        if b is not None:
+            gbs = b / (ms * 1e-3) / 1e9
+            e.update(gbs=round(gbs, 1), frac_of_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
         out[k] = e
     return out
-
-
-def bench_prefill(torch, si, nat, wl, steps, warmup, device):
-    layer, w, x, y, kc, vc, ws = setup_prefill(torch, si, nat, wl, device)
-    run = lambda: layer.prefill(x, y, kc, vc, ws)
-    ms = time_steps(torch, run, steps, warmup)
-    avg = profile_steps(torch, layer, run, steps)
-    flops = layer_flops(wl.cfg, wl.batch, wl.seq_len)
-    total = sum(flops.values())
-    res = dict(ms_per_step=ms, tokens_per_s=wl.batch * wl.seq_len / (ms * 1e-3),
-               layer_tflops=total / (ms * 1e-3) / 1e12, kernels=kernel_table(avg, flops))
-    dominant = max((k for k in avg if stage_flops(flops, k) is not None), key=lambda k: avg[k])
-    res["dominant"] = dominant
-    res["dominant_flops"] = stage_flops(flops, dominant)
-    res["dominant_ms"] = avg[dominant]
-    layer.close()
-    return res
-
-
-def bench_decode(torch, si, nat, wl, steps, warmup, device):
-    cfg = wl.cfg
-    layer, w, x, y, kc, vc, ws = setup_prefill(torch, si, nat, wl, device)
-    g = torch.Generator(device=device).manual_seed(wl.seed + 1)
-    n = wl.cached
-    kc[:, :, :n].copy_(torch.randn(kc[:, :, :n].shape, generator=g, device=device).to(kc.dtype))
-    vc[:, :, :n].copy_(torch.randn(vc[:, :, :n].shape, generator=g, device=device).to(vc.dtype))
-    lens = [n] * wl.batch
-    run = lambda: layer.decode(x, y, lens, kc, vc, ws)
-    ms = time_steps(torch, run, steps, warmup)
-    avg = profile_steps(torch, layer, run, steps)
-    attn_ms = avg["attention_decode_split"]
-    byts = decode_attention_bytes(cfg, wl.batch, n)
-    gbs = byts / (attn_ms * 1e-3) / 1e9
-    layer.close()
-    return dict(ms_per_step=ms, tokens_per_s=wl.batch / (ms * 1e-3), attention_ms=attn_ms,
-                attention_bytes=byts, attention_gbs=gbs, attention_frac_of_hbm_peak=gbs / PEAK_HBM_GBS,
-                kernels={k: {"avg_ms": round(v, 5)} for k, v in avg.items()})
-
-
-def bench_stack(torch, si, nat, wl, steps, warmup, device):
-    """The layer stack with its final RMSNorm: one step runs every layer's prefill in turn, each
-    with its own random-init weights and K/V cache, then the final norm (one shared workspace,
-    one stream)."""
-    cfg = wl.cfg
-    dt = torch.bfloat16
-    g = torch.Generator(device=device).manual_seed(wl.seed)
-    layers, caches = [], []
-    for _ in range(wl.layers):
-        w = {}
-        for name, shape in si.weight_shapes(cfg).items():
-            z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-            w[name] = ((1 + 0.1 * z) if name in si.GAIN_NAMES else 0.02 * z).to(dt)
-        layers.append((nat.Layer(cfg, w), w))
-        kc = torch.zeros((wl.batch, cfg.num_key_value_heads, wl.seq_len, cfg.head_dim), dtype=dt, device=device)
-        caches.append((kc, torch.zeros_like(kc)))
-    gain = (1 + 0.1 * torch.randn(cfg.hidden_size, generator=g, device=device)).to(dt)
-    x = torch.randn((wl.batch, wl.seq_len, cfg.hidden_size), generator=g, device=device).to(dt)
-    bufs = (torch.empty_like(x), torch.empty_like(x))
-    out = torch.empty_like(x)
-    ws = torch.empty(layers[0][0].workspace_size(wl.batch, wl.seq_len, wl.seq_len), dtype=torch.uint8, device=device)
-
-    def run():
-        cur = x
-        for i, ((layer, _), (kc, vc)) in enumerate(zip(layers, caches)):
-            nxt = bufs[i & 1]
-            layer.prefill(cur, nxt, kc, vc, ws)
-            cur = nxt
-        nat.rmsnorm(cur, gain, out, cfg.rms_norm_eps)
-
-    ms = time_steps(torch, run, steps, warmup)
-    flops = sum(layer_flops(cfg, wl.batch, wl.seq_len).values()) * wl.layers
-    for layer, _ in layers:
-        layer.close()
-    return dict(ms_per_step=ms, tokens_per_s=wl.batch * wl.seq_len / (ms * 1e-3),
-                ms_per_layer=ms / wl.layers, stack_tflops=flops / (ms * 1e-3) / 1e12)
-
-
-def cpu_baseline(si, wl, min_s=10.0, budget_s=30.0):
-    """The float64 oracle, untuned, on a bounded sample of the same workload."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    cfg = wl.cfg
-    w = si.layer_weights(cfg, seed=wl.seed)
-    x = si.layer_input(cfg, wl.batch, wl.seq_len, seed=wl.seed)
-    t0 = time.perf_counter()
-    runs = 0
-    while True:
-        oracle.layer_prefill(x, w, cfg)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= min_s or el * (runs + 1) / runs > budget_s:
-            break
-    tok_s = runs * wl.batch * wl.seq_len / el
-    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} full float64 oracle prefill(s) of the {wl.name} workload "
-                      f"(B{wl.batch} x T{wl.seq_len}), {el:.1f} s"}
 
 
 def measured_traffic(kernel, workload):
@@ -252,101 +190,484 @@ def measured_traffic(kernel, workload):
     return None
 
 
+def mfma_roofline(stage, ms, flops, workload):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": stage, "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(stage, workload),
+            "avg_ms": round(ms, 5), "flops_per_launch": flops}
+
+
+# ------------------------------------------------------------------------------ device inputs
+
+def dev(torch, a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(dtype)
+
+
+def device_weights(torch, si, cfg, w_np=None, gen=None):
+    """The layer's weights on the device: the seeded numpy draws when given (so the oracle sees
+    identical values), else drawn on the device with the same distributions."""
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    if w_np is not None:
+        return {k: dev(torch, v, dt) for k, v in w_np.items()}
+    w = {}
+    for name, shape in si.weight_shapes(cfg).items():
+        z = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+        w[name] = ((1 + 0.1 * z) if name in si.GAIN_NAMES else 0.02 * z).to(dt)
+    return w
+
+
+class Prefill:
+    """One layer, its cache and workspace, set up for repeated prefill steps."""
+
+    def __init__(self, torch, nat, cfg, w_dev, x_dev, cap):
+        self.layer = nat.Layer(cfg, w_dev)
+        self.w = w_dev
+        self.x = x_dev
+        self.y = torch.empty_like(x_dev)
+        b = x_dev.shape[0]
+        shape = (b, cfg.num_key_value_heads, cap, cfg.head_dim)
+        self.kc = torch.zeros(shape, dtype=x_dev.dtype, device="cuda")
+        self.vc = torch.zeros_like(self.kc)
+        self.ws = torch.empty(self.layer.workspace_size(b, x_dev.shape[1], cap), dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.layer.prefill(self.x, self.y, self.kc, self.vc, self.ws)
+
+
+# ------------------------------------------------------------------------------ workloads
+
+def bench_prefill(torch, si, nat, wl, steps, warmup, w_np=None, x_np=None):
+    cfg = wl.cfg
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    w = device_weights(torch, si, cfg, w_np, gen)
+    x = dev(torch, x_np, dt) if x_np is not None else \
+        torch.randn((wl.batch, wl.seq_len, cfg.hidden_size), generator=gen, device="cuda").to(dt)
+    run = Prefill(torch, nat, cfg, w, x, wl.seq_len)
+    ms, med = time_steps(torch, run, steps, warmup)
+    avg = profile_steps(torch, [run.layer], run, steps)
+    flops = layer_flops(cfg, wl.batch, wl.seq_len)
+    total = sum(flops.values())
+    res = {"ms_per_step": round(ms, 5), "median_ms_per_step": round(med, 5),
+           "tokens_per_s": round(wl.batch * wl.seq_len / (ms * 1e-3), 1),
+           "layer_tflops": round(total / (ms * 1e-3) / 1e12, 1),
+           "layer_frac_of_bf16_peak": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "steps": steps, "warmup": warmup}
+    if cfg.dtype == "bf16":
+        dom = max((k for k in avg if stage_work(flops, k) is not None), key=lambda k: avg[k])
+        res["roofline"] = mfma_roofline(dom, avg[dom], stage_work(flops, dom), wl.name)
+        res["kernels"] = kernel_table(avg, flops)
+    else:
+        res["kernels"] = kernel_table(avg)
+    y = run.y.float().cpu().numpy()
+    run.layer.close()
+    return res, y
+
+
+def bench_stack(torch, si, nat, wl, steps, warmup):
+    """The layer stack with its final RMSNorm: one step runs every layer's prefill in turn, each
+    with its own random-init weights and K/V cache, then the final norm (one shared workspace,
+    one stream)."""
+    cfg = wl.cfg
+    dt = torch.bfloat16
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    layers, caches = [], []
+    for _ in range(wl.layers):
+        w = device_weights(torch, si, cfg, None, gen)
+        layers.append((nat.Layer(cfg, w), w))
+        kc = torch.zeros((wl.batch, cfg.num_key_value_heads, wl.seq_len, cfg.head_dim), dtype=dt, device="cuda")
+        caches.append((kc, torch.zeros_like(kc)))
+    gain = (1 + 0.1 * torch.randn(cfg.hidden_size, generator=gen, device="cuda")).to(dt)
+    x = torch.randn((wl.batch, wl.seq_len, cfg.hidden_size), generator=gen, device="cuda").to(dt)
+    bufs = (torch.empty_like(x), torch.empty_like(x))
+    out = torch.empty_like(x)
+    ws = torch.empty(layers[0][0].workspace_size(wl.batch, wl.seq_len, wl.seq_len), dtype=torch.uint8, device="cuda")
+
+    def run():
+        cur = x
+        for i, ((layer, _), (kc, vc)) in enumerate(zip(layers, caches)):
+            nxt = bufs[i & 1]
+            layer.prefill(cur, nxt, kc, vc, ws)
+            cur = nxt
+        nat.rmsnorm(cur, gain, out, cfg.rms_norm_eps)
+
+    ms, med = time_steps(torch, run, steps, warmup)
+    avg = profile_steps(torch, [l for l, _ in layers], run, max(1, steps // 2))
+    flops = layer_flops(cfg, wl.batch, wl.seq_len)
+    total = sum(flops.values()) * wl.layers
+    dom = max((k for k in avg if stage_work(flops, k) is not None), key=lambda k: avg[k])
+    for layer, _ in layers:
+        layer.close()
+    return {"ms_per_step": round(ms, 5), "median_ms_per_step": round(med, 5),
+            "tokens_per_s": round(wl.batch * wl.seq_len / (ms * 1e-3), 1),
+            "ms_per_layer": round(ms / wl.layers, 5),
+            "stack_tflops": round(total / (ms * 1e-3) / 1e12, 1),
+            "stack_frac_of_bf16_peak": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "steps": steps, "warmup": warmup,
+            "roofline": mfma_roofline(dom, avg[dom], stage_work(flops, dom), wl.name),
+            "kernels": kernel_table(avg, flops)}
+
+
+def bench_decode(torch, si, nat, wl, steps, warmup, w_np=None):
+    cfg = wl.cfg
+    dt = torch.bfloat16
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    w = device_weights(torch, si, cfg, w_np, gen)
+    n = wl.cached
+    cap = n + 1
+    x = torch.randn((wl.batch, 1, cfg.hidden_size), generator=gen, device="cuda").to(dt)
+    run = Prefill(torch, nat, cfg, w, x, cap)
+    for c in (run.kc, run.vc):
+        for b in range(wl.batch):
+            c[b, :, :n].copy_(torch.randn(c[b, :, :n].shape, generator=gen, device="cuda").to(dt))
+    lens = [n] * wl.batch
+    step = lambda: run.layer.decode(run.x, run.y, lens, run.kc, run.vc, run.ws)
+    ms, med = time_steps(torch, step, steps, warmup)
+    avg = profile_steps(torch, [run.layer], step, steps)
+    run.layer.close()
+    kv = decode_attention_bytes(cfg, wl.batch, n)
+    attn_ms = avg["attention_decode_split"] + avg["attention_decode_combine"]
+    gbs = kv / (attn_ms * 1e-3) / 1e9
+    split_gbs = kv / (avg["attention_decode_split"] * 1e-3) / 1e9
+    layer_bytes = kv + decode_weight_bytes(cfg)
+    return {"ms_per_step": round(ms, 5), "median_ms_per_step": round(med, 5),
+            "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "steps": steps, "warmup": warmup,
+            "roofline": {"bound": "hbm", "kernel": "attention_decode_split + attention_decode_combine",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("attention_decode_split", wl.name),
+                         "avg_ms": round(attn_ms, 5), "bytes_per_launch": kv,
+                         "split_kernel_only": {"avg_ms": round(avg["attention_decode_split"], 5),
+                                               "achieved": round(split_gbs, 1),
+                                               "frac": round(split_gbs / PEAK_HBM_GBS, 4)}},
+            "layer_bytes": layer_bytes,
+            "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+            "layer_frac_of_hbm_peak": round(layer_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernels": kernel_table(avg, byts=decode_skinny_bytes(cfg))}
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas}
+
+
+def parity(got, ref, fp32=False):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    out = {"max_abs": float(d.max()), "mean_rel": float(d.sum() / max(np.abs(ref).sum(), 1e-300)),
+           "rms_ref": round(rms, 4), "elements": int(d.size)}
+    if fp32:
+        out.update(max_abs_bar=F32_MAX_ABS, ok=bool(out["max_abs"] <= F32_MAX_ABS))
+    else:
+        bar = BF16_MAX_ABS * max(1.0, rms)
+        out.update(max_abs_bar=round(bar, 5), mean_rel_bar=BF16_MEAN_REL,
+                   ok=bool(out["max_abs"] <= bar and out["mean_rel"] <= BF16_MEAN_REL))
+    return out
+
+
+def oracle_prefill_baseline(oracle, wl, w, x, y_gpu, min_s=0.0, note=""):
+    """Full float64 oracle prefills of the workload's input, repeated until min_s have passed."""
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        ref = oracle.layer_prefill(x, w, wl.cfg)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            break
+    tok = runs * wl.batch * wl.seq_len
+    return {"value": round(tok / el, 2), "unit": "tokens/s", "seconds": round(el, 3),
+            "sample": f"{runs} full float64 oracle prefill(s) of {wl.name} (B{wl.batch} x T{wl.seq_len}){note}",
+            "parity_vs_gpu": parity(y_gpu, ref["y"], fp32=wl.cfg.dtype == "f32")}
+
+
+def run_cpu_baselines(torch, si, nat, wls, gpu_y, inputs):
+    """The oracle as it stands (plain float64 numpy), on the host cores of the GPU machine, on the
+    same inputs the GPU consumed: each workload's sample is stated in its record."""
+    import oracle
+    out = {}
+    if "c4" in wls:
+        wl = wls["c4"]
+        w, x = inputs["c4"]
+        print(f"[bench] cpu baseline: {wl.name}", file=sys.stderr, flush=True)
+        out[wl.name] = oracle_prefill_baseline(oracle, wl, w, x, gpu_y["c4"])
+    if "c2" in wls:
+        wl = wls["c2"]
+        w, x = inputs["c2"]
+        print(f"[bench] cpu baseline: {wl.name}", file=sys.stderr, flush=True)
+        out[wl.name] = oracle_prefill_baseline(oracle, wl, w, x, gpu_y["c2"], min_s=3.0)
+    if "c1" in wls:
+        wl = wls["c1"]
+        w, x = inputs["c1"]
+        out[wl.name] = oracle_prefill_baseline(oracle, wl, w, x, gpu_y["c1"], min_s=1.0)
+    if "c3" in wls:
+        # one layer of the stack (layer 0's seeded weights on the stack's B4 x T4096 input),
+        # its time scaled by the 28 layers; the final norm's time is negligible beside it
+        wl = wls["c3"]
+        print(f"[bench] cpu baseline: {wl.name} (layer 0)", file=sys.stderr, flush=True)
+        w, x = inputs["c3"]
+        t0 = time.perf_counter()
+        ref = oracle.layer_prefill(x, w, wl.cfg)
+        el = time.perf_counter() - t0
+        out[wl.name] = {"value": round(wl.batch * wl.seq_len / (el * wl.layers), 2), "unit": "tokens/s",
+                        "seconds": round(el, 3), "scaled_seconds": round(el * wl.layers, 3),
+                        "sample": f"one float64 oracle layer (layer 0 of the stack, B{wl.batch} x T{wl.seq_len}) "
+                                  f"timed once, its time multiplied by {wl.layers} layers",
+                        "parity_vs_gpu": parity(gpu_y["c3"], ref["y"])}
+    if "c5" in wls:
+        # two of the sixteen sequences, each with its own seeded 32768-key cache; tokens/s from
+        # their time (the oracle treats sequences independently)
+        wl = wls["c5"]
+        print(f"[bench] cpu baseline: {wl.name} (2 sequences)", file=sys.stderr, flush=True)
+        w, x, kc, vc, lens, y = inputs["c5"]
+        t0 = time.perf_counter()
+        ref, _, _ = oracle.layer_decode(x, w, wl.cfg, kc, vc, lens)
+        el = time.perf_counter() - t0
+        out[wl.name] = {"value": round(len(lens) / el, 3), "unit": "tokens/s", "seconds": round(el, 3),
+                        "sample": f"float64 oracle decode of {len(lens)} of the {wl.batch} sequences, "
+                                  f"each over {wl.cached} cached keys plus the new one",
+                        "parity_vs_gpu": parity(y, ref)}
+    return out
+
+
+def decode_parity_inputs(torch, si, nat, wl, w_np, nseq=2):
+    """A decode call on `nseq` sequences with seeded caches of the workload's length (same
+    kernels and launch shapes per sequence as the timed batch), for the oracle to check."""
+    cfg = wl.cfg
+    n = wl.cached
+    cap = n + 1
+    hkv, d = cfg.num_key_value_heads, cfg.head_dim
+    kc = np.zeros((nseq, hkv, cap, d), np.float32)
+    vc = np.zeros((nseq, hkv, cap, d), np.float32)
+
+    def sink(b, h, kb, vb):
+        kc[b, h, :n] = kb
+        vc[b, h, :n] = vb
+
+    si.fill_decode_cache(cfg, nseq, n, sink, seed=wl.seed)
+    x = si.layer_input(cfg, nseq, 1, seed=wl.seed)
+    dt = torch.bfloat16
+    w = device_weights(torch, si, cfg, w_np)
+    layer = nat.Layer(cfg, w)
+    kd, vd = dev(torch, kc, dt), dev(torch, vc, dt)
+    xd = dev(torch, x, dt)
+    yd = torch.empty_like(xd)
+    ws = torch.empty(layer.workspace_size(nseq, 1, cap), dtype=torch.uint8, device="cuda")
+    layer.decode(xd, yd, [n] * nseq, kd, vd, ws)
+    torch.cuda.synchronize()
+    y = yd.float().cpu().numpy()
+    layer.close()
+    del kd, vd
+    return w_np, x, kc, vc, [n] * nseq, y
+
+
+# ------------------------------------------------------------------------------ rocprof summaries
+
+def _short(name):
+    import re
+    name = re.sub(r"\(anonymous namespace\)::|q3::", "", name)
+    return re.sub(r"^void ", "", name)
+
+
+def summarize_rocprof(db, mode):
+    """Markdown table from a rocprofv3 database of this benchmark: 'trace' (durations per
+    kernel and grid), 'traffic' (FETCH_SIZE / WRITE_SIZE per dispatch), or 'mfma' (MFMA
+    utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (4 * CUs * GRBM_GUI_ACTIVE), and the clock
+    GRBM_GUI_ACTIVE / duration)."""
+    import collections
+    import sqlite3
+    c = sqlite3.connect(db).cursor()
+    lines = []
+    if mode == "trace":
+        rows = c.execute("select name, grid_x, grid_y, grid_z, workgroup_x, start, end from kernels").fetchall()
+        agg = collections.defaultdict(list)
+        for n, gx, gy, gz, wx, s, e in rows:
+            agg[(_short(n), gx // max(wx, 1), gy, gz)].append((e - s) / 1e3)
+        lines.append("| kernel | grid (workgroups) | calls | avg us | median us |")
+        lines.append("|---|---|---|---|---|")
+        for (n, gx, gy, gz), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+            v = sorted(v)
+            lines.append(f"| `{n}` | ({gx}, {gy}, {gz}) | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} |")
+        return "\n".join(lines)
+    rows = c.execute("select dispatch_id, kernel_name, grid_size_x, grid_size_y, grid_size_z, workgroup_size_x, "
+                     "counter_name, value from counters_collection").fetchall()
+    disp = collections.defaultdict(lambda: collections.defaultdict(float))
+    key = {}
+    for di, n, gx, gy, gz, wx, cn, v in rows:
+        disp[di][cn] += v
+        key[di] = (_short(n), gx // max(wx, 1), gy, gz)
+    dur = {}
+    try:
+        for di, s, e in c.execute("select dispatch_id, start, end from kernels").fetchall():
+            dur[di] = (e - s)
+    except sqlite3.Error:
+        pass
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for di, cs in disp.items():
+        for cn, v in cs.items():
+            agg[key[di]][cn].append(v)
+        if di in dur and "GRBM_GUI_ACTIVE" in cs and dur[di] > 0:
+            agg[key[di]]["_mhz"].append(cs["GRBM_GUI_ACTIVE"] / dur[di] * 1e3)
+            agg[key[di]]["_us"].append(dur[di] / 1e3)
+    avg = lambda v: sum(v) / len(v) if v else float("nan")
+    if mode == "traffic":
+        lines.append("| kernel | grid (workgroups) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |")
+        lines.append("|---|---|---|---|---|")
+        for k in sorted(agg, key=lambda k: -avg(agg[k].get("FETCH_SIZE", [0]))):
+            a = agg[k]
+            n = max(len(a.get("FETCH_SIZE", [])), len(a.get("WRITE_SIZE", [])))
+            lines.append(f"| `{k[0]}` | {k[1:]} | {n} | {avg(a.get('FETCH_SIZE', [])):.1f} | "
+                         f"{avg(a.get('WRITE_SIZE', [])):.1f} |")
+        return "\n".join(lines)
+    lines.append("| kernel | grid (workgroups) | dispatches | avg us | MFMA busy % | clock MHz | "
+                 "SQ_BUSY_CYCLES / GRBM_GUI_ACTIVE | bf16 MFMA MOPS |")
+    lines.append("|---|---|---|---|---|---|---|---|")
+    for k in sorted(agg, key=lambda k: -avg(agg[k].get("_us", [0])) * len(agg[k].get("_us", [0]))):
+        a = agg[k]
+        gui = avg(a.get("GRBM_GUI_ACTIVE", []))
+        util = 100.0 * avg(a.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / (4 * CU_COUNT * gui) if gui else float("nan")
+        sqb = avg(a.get("SQ_BUSY_CYCLES", [])) / gui if gui else float("nan")
+        lines.append(f"| `{k[0]}` | {k[1:]} | {len(a.get('GRBM_GUI_ACTIVE', []))} | {avg(a.get('_us', [])):.2f} | "
+                     f"{util:.1f} | {avg(a.get('_mhz', [])):.0f} | {sqb:.2f} | "
+                     f"{avg(a.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', [])):.4g} |")
+    return "\n".join(lines)
+
+
+# ------------------------------------------------------------------------------ main
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 8B prefill, 28-layer stack and 32K decode measurements")
-    ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of the 8B prefill / decode runs")
+    ap.add_argument("--workloads", default="c4,c2,c3,c5,c1",
+                    help="comma list of c1..c5 (c4, the headline, always runs)")
     ap.add_argument("--settle", type=float, default=SETTLE_S,
                     help="seconds of untimed steps before each workload's warmup steps (clock settling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DB", help="print a markdown summary of a rocprofv3 database")
+    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "mfma"])
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        print(summarize_rocprof(args.summarize_rocprof, args.mode))
+        return
     global settle_seconds
     settle_seconds = max(0.0, args.settle)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path.", file=sys.stderr)
+              "multi-GPU path: the layer's kernels run on one GPU's share of the work.", file=sys.stderr)
         sys.exit(2)
+    keys = ["c4"] + [k.strip() for k in args.workloads.split(",") if k.strip() and k.strip() != "c4"]
+    for k in keys:
+        if k not in SHORT:
+            ap.error(f"unknown workload {k}")
 
     import torch
     import seeded_inputs as si
     from transformer_decoder_layer_rmsnorm_amd import _native as nat
     nat.lib()
-    device = "cuda:0"
     torch.cuda.set_device(0)
+    wls = {k: si.WORKLOADS[SHORT[k]] for k in keys}
+    cpu = not args.no_cpu_baseline
 
     calib = None
     if args.copy_calibration:
         n = 256 << 20
-        src = torch.ones(n, dtype=torch.uint8, device=device)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        ms = time_steps(torch, lambda: dst.copy_(src), 5, 1)
+        ms, _ = time_steps(torch, lambda: dst.copy_(src), 5, 1)
         calib = {"bytes_read": n, "bytes_written": n, "avg_ms": round(ms, 4),
                  "gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
         del src, dst
 
-    wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
-    print(f"[bench] {wl.name}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
-    res = bench_prefill(torch, si, nat, wl, args.steps, args.warmup, device)
-    dom_tf = res["dominant_flops"] / (res["dominant_ms"] * 1e-3) / 1e12
+    gpu_y, inputs, records = {}, {}, {}
+    w8 = None
+    for k in keys:
+        wl = wls[k]
+        print(f"[bench] {wl.name}", file=sys.stderr, flush=True)
+        if k in ("c1", "c2", "c4"):
+            w_np = x_np = None
+            if cpu or k == "c1":
+                w_np = si.layer_weights(wl.cfg, seed=wl.seed)
+                x_np = si.layer_input(wl.cfg, wl.batch, wl.seq_len, seed=wl.seed)
+                inputs[k] = (w_np, x_np)
+                if k == "c4":
+                    w8 = w_np
+            steps = args.steps if k != "c1" else max(args.steps, 50)
+            res, y = bench_prefill(torch, si, nat, wl, steps, args.warmup, w_np, x_np)
+            gpu_y[k] = y
+            records[k] = res
+        elif k == "c3":
+            records[k] = bench_stack(torch, si, nat, wl, max(2, args.steps // 10), 1)
+            if cpu:
+                w_np = si.layer_weights(wl.cfg, layer=0, seed=wl.seed)
+                x_np = si.layer_input(wl.cfg, wl.batch, wl.seq_len, seed=wl.seed)
+                inputs[k] = (w_np, x_np)
+                _, gpu_y[k] = bench_prefill(torch, si, nat, wl, 1, 0, w_np, x_np)
+        elif k == "c5":
+            records[k] = bench_decode(torch, si, nat, wl, args.steps, args.warmup, w8)
+            if cpu:
+                w_np = w8 if w8 is not None else si.layer_weights(wl.cfg, seed=wl.seed)
+                inputs[k] = decode_parity_inputs(torch, si, nat, wl, w_np)
+        torch.cuda.empty_cache()
+
+    head = records["c4"]
+    wl4 = wls["c4"]
     line = {
         "metric": METRIC,
-        "value": round(res["tokens_per_s"], 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_s": settle_seconds,
-        "ms_per_step": round(res["ms_per_step"], 5),
+        "ms_per_step": head["ms_per_step"],
+        "median_ms_per_step": head["median_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len,
-                   "hidden_size": wl.cfg.hidden_size, "heads": [wl.cfg.num_attention_heads,
-                                                                wl.cfg.num_key_value_heads],
-                   "head_dim": wl.cfg.head_dim, "intermediate_size": wl.cfg.intermediate_size},
-        "roofline": {"bound": "mfma", "kernel": res["dominant"], "achieved": round(dom_tf, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(res["dominant"], wl.name)},
-        "layer_tflops": round(res["layer_tflops"], 1),
-        "layer_frac_of_bf16_peak": round(res["layer_tflops"] / PEAK_BF16_TFLOPS, 4),
-        "kernels": res["kernels"],
+        "data": "synthetic (seeded random-init weights and inputs of the workload's shapes)",
+        "config": {"workload": wl4.name, "batch": wl4.batch, "seq_len": wl4.seq_len,
+                   "hidden_size": wl4.cfg.hidden_size,
+                   "heads": [wl4.cfg.num_attention_heads, wl4.cfg.num_key_value_heads],
+                   "head_dim": wl4.cfg.head_dim, "intermediate_size": wl4.cfg.intermediate_size},
+        "roofline": head["roofline"],
+        "layer_tflops": head["layer_tflops"],
+        "layer_frac_of_bf16_peak": head["layer_frac_of_bf16_peak"],
+        "kernels": head["kernels"],
+        "workloads": {wls[k].name: records[k] for k in keys if k != "c4"},
     }
-    if not args.no_extra:
-        wl4 = si.WORKLOADS["qwen3-8b-layer-prefill"]
-        print(f"[bench] {wl4.name}", file=sys.stderr, flush=True)
-        r4 = bench_prefill(torch, si, nat, wl4, args.extra_steps, 3, device)
-        line["qwen3_8b_layer_prefill"] = {
-            "tokens_per_s": round(r4["tokens_per_s"], 1), "ms_per_step": round(r4["ms_per_step"], 4),
-            "layer_tflops": round(r4["layer_tflops"], 1),
-            "layer_frac_of_bf16_peak": round(r4["layer_tflops"] / PEAK_BF16_TFLOPS, 4), "kernels": r4["kernels"]}
-        wl3 = si.WORKLOADS["qwen3-0.6b-stack28-prefill"]
-        print(f"[bench] {wl3.name}", file=sys.stderr, flush=True)
-        r3 = bench_stack(torch, si, nat, wl3, max(2, args.extra_steps // 2), 1, device)
-        line["qwen3_0p6b_stack28_prefill"] = {
-            "tokens_per_s": round(r3["tokens_per_s"], 1), "ms_per_step": round(r3["ms_per_step"], 4),
-            "ms_per_layer": round(r3["ms_per_layer"], 4), "stack_tflops": round(r3["stack_tflops"], 1),
-            "stack_frac_of_bf16_peak": round(r3["stack_tflops"] / PEAK_BF16_TFLOPS, 4)}
-        wl5 = si.WORKLOADS["qwen3-8b-layer-decode-32k"]
-        print(f"[bench] {wl5.name}", file=sys.stderr, flush=True)
-        r5 = bench_decode(torch, si, nat, wl5, 2 * args.extra_steps, 5, device)
-        line["decode_32k"] = {
-            "tokens_per_s": round(r5["tokens_per_s"], 1), "ms_per_step": round(r5["ms_per_step"], 4),
-            "roofline": {"bound": "hbm", "kernel": "attention_decode_split", "achieved": round(r5["attention_gbs"], 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(r5["attention_frac_of_hbm_peak"], 4),
-                         "traffic": measured_traffic("attention_decode_split", wl5.name)},
-            "kernels": r5["kernels"]}
     if calib:
         line["copy_calibration"] = calib
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(si, wl)
+    if cpu:
+        base = run_cpu_baselines(torch, si, nat, wls, gpu_y, inputs)
+        info = cpu_info()
+        head_b = base.pop(wl4.name)
+        line["cpu_baseline"] = {"value": head_b["value"], "unit": head_b["unit"],
+                                "cores": info["blas_threads"] or info["affinity_cores"], "kind": "oracle",
+                                "sample": head_b["sample"], "seconds": head_b["seconds"],
+                                "parity_vs_gpu": head_b["parity_vs_gpu"], **info,
+                                "workloads": base}
     print(json.dumps(line), flush=True)
 
 

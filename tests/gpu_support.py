@@ -187,3 +187,78 @@ def check_decode_steps(gl, ws, lens, kd, vd):
         att = oracle.gqa_causal_attention(it["qhat"][i], kdn[i, :, : n + 1], vdn[i, :, : n + 1],
                                           np.array([n]), np.arange(n + 1))
         assert_bf16_parity(it["attn"][i], att.transpose(1, 0, 2).reshape(1, hq * d), f"decode attention, {n + 1} keys")
+
+
+# ---------------------------------------------------------------- full-tensor checks at full size
+
+def _pool_map(fn, items, workers=8):
+    """Map fn over items on a thread pool (numpy releases the GIL in its array work)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, min(workers, len(items)))) as pool:
+        return list(pool.map(fn, items))
+
+
+def oracle_attention_per_head(qhat, kc, vc, q_pos, k_pos, workers=8):
+    """oracle.gqa_causal_attention evaluated head by head on a thread pool (the same
+    definition; each call sees one query head and the KV head it reads).
+    qhat [Hq, T, D], kc / vc [Hkv, S, D] -> [Hq, T, D]."""
+    hq, hkv = qhat.shape[0], kc.shape[0]
+    g = hq // hkv
+    outs = _pool_map(lambda h: oracle.gqa_causal_attention(qhat[h:h + 1], kc[h // g: h // g + 1],
+                                                           vc[h // g: h // g + 1], q_pos, k_pos)[0],
+                     list(range(hq)), workers)
+    return np.stack(outs)
+
+
+def oracle_layer_prefill_parallel(x, w, cfg, workers=4):
+    """oracle.layer_prefill with its sequences evaluated on a thread pool (the oracle treats
+    sequences independently, so this is the same result)."""
+    parts = _pool_map(lambda b: oracle.layer_prefill(x[b:b + 1], w, cfg), list(range(x.shape[0])), workers)
+    return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+
+
+def check_prefill_stages_full(gl, x, y_dev, kc_dev, vc_dev, ws, what):
+    """Every element of every stage of a prefill on an empty cache (positions 0..T-1), each
+    stage fed the GPU's own input for it (teacher forcing) from the workspace:
+      h = rmsnorm(x);  qhat, khat, v from h through the projections, QK-norm and RoPE (the
+      fused QKV epilogue never stores the raw projections, so this step starts at h);
+      attn from the GPU's qhat and cache;  x1 = x + attn Wo^T (fp32);  h2 = rmsnorm(x1);
+      act = silu(h2 Wg^T) * (h2 Wu^T);  y = x1 + act Wd^T.
+    Returns the stage metrics (raw max-abs included)."""
+    cfg, w = gl.cfg, gl.w_np
+    b, t, _ = x.shape
+    hq, hkv, d = cfg.num_attention_heads, cfg.num_key_value_heads, cfg.head_dim
+    eps = cfg.rms_norm_eps
+    it = gl.intermediates(ws, b, t)
+    y = to_np(y_dev)
+    kcn, vcn = to_np(kc_dev), to_np(vc_dev)
+    pos = np.arange(t)
+    f64 = lambda a: np.asarray(a, np.float64)
+    wqkv = np.concatenate([w["q_proj"], w["k_proj"], w["v_proj"]]).astype(np.float64)
+    stats = {}
+    for s in range(b):
+        tag = f"{what} seq {s}"
+        assert_rounded(it["h"][s], oracle.rmsnorm(x[s], w["input_layernorm"], eps), f"{tag}: rmsnorm_input")
+        qhat, khat, v = oracle_qk_from_proj(it["h"][s] @ wqkv.T, w, cfg, pos)
+        assert_rounded(it["qhat"][s], qhat, f"{tag}: q (QKV + QK-norm + RoPE)")
+        assert_rounded(kcn[s, :, :t], khat, f"{tag}: k cache (QKV + QK-norm + RoPE)")
+        assert_rounded(vcn[s, :, :t], v, f"{tag}: v cache (QKV)")
+        del qhat, khat, v
+        log(f"  {tag}: attention, {hq} heads")
+        att = oracle_attention_per_head(it["qhat"][s], kcn[s, :, :t], vcn[s, :, :t], pos, pos)
+        stats[f"attn{s}"] = assert_bf16_parity(it["attn"][s], att.transpose(1, 0, 2).reshape(t, hq * d),
+                                               f"{tag}: attention")
+        del att
+        x1 = x[s] + it["attn"][s] @ f64(w["o_proj"]).T
+        d1 = np.abs(it["x1"][s] - x1)
+        log(f"  {tag}: x1 (fp32) max_abs {d1.max():.3g}")
+        np.testing.assert_allclose(it["x1"][s], x1, rtol=1e-5, atol=2e-5)
+        del x1, d1
+        assert_rounded(it["h2"][s], oracle.rmsnorm(it["x1"][s], w["post_attention_layernorm"], eps),
+                       f"{tag}: rmsnorm_post")
+        h2 = it["h2"][s]
+        act = oracle.silu(h2 @ f64(w["gate_proj"]).T) * (h2 @ f64(w["up_proj"]).T)
+        assert_rounded(it["act"][s], act, f"{tag}: gate/up + SwiGLU")
+        del act
+        assert_rounded(y[s], it["x1"][s] + it["act"][s] @ f64(w["down_proj"]).T, f"{tag}: down + residual")
+    return stats

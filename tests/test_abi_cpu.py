@@ -98,6 +98,19 @@ def test_create_accepts_rope_and_norm_variants():
         == nat.QWEN3_ERR_INVALID_ARGUMENT
 
 
+def test_create_accepts_bf16_hidden_above_4096():
+    """hidden 5120 (a family width): every bf16 kernel has a form for rows over 4096 wide, so
+    create and workspace sizing accept it (the kernels themselves run in the GPU tests)."""
+    cfg = si.LayerConfig(**{**si.QWEN3_0P6B.__dict__, "hidden_size": 5120, "num_attention_heads": 64,
+                            "intermediate_size": 25600})
+    st, h = create(cfg)
+    assert st == nat.QWEN3_OK, err()
+    n = ctypes.c_size_t()
+    assert nat.lib().qwen3_layer_workspace_size(h, 1, 2048, 2048, ctypes.byref(n)) == nat.QWEN3_OK, err()
+    assert n.value >= 2048 * 5120 * (2 + 4 + 2)
+    nat.lib().qwen3_layer_destroy(h)
+
+
 def test_create_rejects_null_and_misaligned_weights():
     w = fake_weights()
     w.q_norm = None

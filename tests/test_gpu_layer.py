@@ -132,6 +132,36 @@ def test_bf16_layer_matches_oracle(hq, hkv, b, t):
     assert_bf16_parity(to_np(y), oracle.layer_prefill(x, gl.w_np, cfg)["y"], "y")
 
 
+@pytest.mark.parametrize("t", [1100, 700])
+def test_bf16_hidden_5120_layer(t):
+    """hidden 5120, a width of the family above 4096 (16 / 8 heads, intermediate 1024).
+    T = 1100: the fused QKV epilogue on 128 x 128 tiles, fed by the input RMSNorm that also
+    writes the RoPE table, in its form for rows over 4096 wide.  T = 700: too few output tiles
+    for o_proj, whose K range is split and whose slabs the post-attention RMSNorm sums, in its
+    form for rows over 4096 wide; down split-K with the residual-sum pass.  Then one decode
+    step on the prefilled cache (skinny GEMMs with K = 5120)."""
+    cfg = small_bf16_cfg(hq=16, hkv=8, hidden=5120, inter=1024)
+    log(f"bf16 layer hidden 5120, B1 T{t}")
+    gl = GpuLayer.seeded(cfg, seed=t)
+    x = si.layer_input(cfg, 1, t + 1, seed=t)
+    cap = t + 1
+    kc, vc = gl.alloc_cache(1, cap)
+    y, kc, vc, ws = gl.prefill(to_dev(x[:, :t], cfg), cap=cap, caches=(kc, vc))
+    ref = oracle.layer_prefill(x[:, :t], gl.w_np, cfg)
+    it = gl.intermediates(ws, 1, t)
+    eps = cfg.rms_norm_eps
+    assert_rounded(it["h"][0], oracle.rmsnorm(x[0, :t], gl.w_np["input_layernorm"], eps), "rmsnorm_input (5120 wide)")
+    assert_rounded(it["h2"][0], oracle.rmsnorm(it["x1"][0], gl.w_np["post_attention_layernorm"], eps),
+                   "rmsnorm_post (5120 wide)")
+    x1 = x[0, :t] + it["attn"][0] @ gl.w_np["o_proj"].T.astype(np.float64)
+    np.testing.assert_allclose(it["x1"][0], x1, rtol=1e-5, atol=2e-5)
+    assert_bf16_parity(to_np(y), ref["y"], "y")
+    assert_bf16_parity(to_np(kc)[:, :, :t], ref["khat"], "k cache")
+    yd, _ = gl.decode(to_dev(x[:, t:], cfg), [t], kc, vc)
+    refd = oracle.layer_prefill_rows(x, gl.w_np, cfg, [(0, t)])
+    assert_bf16_parity(to_np(yd)[0, 0], refd[0], "decode row at position T")
+
+
 def test_bf16_causality_bit_exact():
     cfg = small_bf16_cfg()
     gl = GpuLayer.seeded(cfg, seed=9)

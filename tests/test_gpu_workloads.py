@@ -1,12 +1,18 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
   * 0.6B-shaped layer, B1 T2048: every output element against the oracle.
-  * 8B-shaped layer, B1 T8192: sampled rows (the oracle computes keys/values for all
-    tokens and the rest only for the sampled rows).
+  * 8B-shaped layer, B1 T8192: every element of every stage, teacher-forced (each stage fed
+    the GPU's own input for it), and every output element against the whole oracle layer.
   * 8B-shaped decode, 16 sequences on 32768 cached keys: every output row.
-  * 0.6B-shaped 28-layer stack, B4 T4096: each layer teacher-forced (the oracle layer fed
-    the GPU's bf16 input of that layer) on sampled rows, plus the final norm; the same
-    stack in fp32 end to end at a small length; the bf16 end-to-end drift is reported.
+  * 0.6B-shaped 28-layer stack, B4 T4096: every output element of every layer against the
+    oracle layer fed the GPU's bf16 input of that layer (teacher-forced), every stage of the
+    first and last layers, and the final norm; the same stack in fp32 end to end at a small
+    length; the bf16 end-to-end drift is reported.
+
+Pass rule for bf16 outputs ("17. A modern architecture: Qwen3", section Why parity tests matter
+now: random weights exercise every path, so a close match on them is the evidence): mean
+relative error <= 5e-3 and max-abs <= 3e-2 * max(1, rms(ref)); the raw max-abs is logged beside
+the scaled bar.
 """
 import numpy as np
 import pytest
@@ -15,7 +21,8 @@ import torch
 import oracle
 import seeded_inputs as si
 from gpu_support import (GpuLayer, assert_bf16_parity, assert_f32_parity, assert_rounded, bf16_metrics,
-                         check_decode_steps, log, to_dev, to_np)
+                         check_decode_steps, check_prefill_stages_full, log, oracle_layer_prefill_parallel, to_dev,
+                         to_np)
 from transformer_decoder_layer_rmsnorm_amd import _native as nat
 
 pytestmark = pytest.mark.gpu
@@ -35,20 +42,25 @@ def test_qwen3_0p6b_layer_prefill_every_row():
     assert_bf16_parity(to_np(kc), ref["khat"], "k cache")
 
 
-def test_qwen3_8b_layer_prefill_sampled_rows():
+@pytest.mark.timeout(900)
+def test_qwen3_8b_layer_prefill_every_element():
+    """8B-shaped layer, B1 T8192: the QKV and gate/up projections on 256 x 256 ping-pong tiles
+    (fused QK-norm / RoPE / cache epilogue; SwiGLU epilogue), o_proj and down on 256 x 256
+    ping-pong tiles whose residual epilogues go through LDS, attention with 4 query heads per
+    workgroup."""
     wl = si.WORKLOADS["qwen3-8b-layer-prefill"]
     cfg = wl.cfg
     log(f"{wl.name}: B{wl.batch} T{wl.seq_len}")
     gl = GpuLayer.seeded(cfg, seed=wl.seed)
     x = si.layer_input(cfg, wl.batch, wl.seq_len, seed=wl.seed)
     y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
-    rng = np.random.default_rng(1)
-    ts = sorted(set([0, 1, 31, 32, 63, 64, 127, 128, 1000, 2047, 4095, 4096, 6000, 8190, 8191] +
-                    list(rng.integers(0, wl.seq_len, 9))))
-    rows = [(0, t) for t in ts]
-    ref = oracle.layer_prefill_rows(x, gl.w_np, cfg, rows)
-    got = to_np(y)[0, ts]
-    assert_bf16_parity(got, ref, f"y at {len(ts)} sampled rows")
+    log("  GPU done; teacher-forced stages")
+    check_prefill_stages_full(gl, x, y, kc, vc, ws, "8B layer")
+    log("  whole oracle layer")
+    ref = oracle.layer_prefill(x, gl.w_np, cfg)
+    assert_bf16_parity(to_np(y), ref["y"], "y, every element (whole oracle layer)")
+    assert_bf16_parity(to_np(kc), ref["khat"], "k cache, every element")
+    assert_bf16_parity(to_np(vc), ref["v"], "v cache, every element")
 
 
 def test_qwen3_8b_layer_prefill_ragged_tail_rows():
@@ -110,7 +122,11 @@ def test_qwen3_8b_decode_32k_every_row():
     check_decode_steps(gl, ws, [n] * b, kd, vd)
 
 
+@pytest.mark.timeout(900)
 def test_qwen3_0p6b_stack28_teacher_forced():
+    """28 layers on B4 T4096 (M = 16384): QKV and gate/up on 256 x 256 ping-pong tiles at
+    K = 1024, o_proj and down on 256 x 256 ping-pong tiles with residual epilogues through LDS,
+    attention with two query heads per workgroup and whole 64-key tiles per wave."""
     wl = si.WORKLOADS["qwen3-0.6b-stack28-prefill"]
     cfg = wl.cfg
     b, t = wl.batch, wl.seq_len
@@ -118,7 +134,6 @@ def test_qwen3_0p6b_stack28_teacher_forced():
     x = si.layer_input(cfg, b, t, seed=wl.seed)
     cur = to_dev(x, cfg)
     kc = vc = ws = None
-    rng = np.random.default_rng(2)
     worst = None
     for layer in range(wl.layers):
         gl = GpuLayer.seeded(cfg, layer=layer, seed=wl.seed)
@@ -126,22 +141,22 @@ def test_qwen3_0p6b_stack28_teacher_forced():
             kc, vc = gl.alloc_cache(b, t)
             ws = gl.workspace(b, t, t)
         y, *_ = gl.prefill(cur, caches=(kc, vc), ws=ws)
-        seqs = [layer % b, (layer + 2) % b]
-        rows = [(s, int(r)) for s in seqs for r in [0, t - 1, rng.integers(1, t - 1)]]
         xin = to_np(cur)
-        ref = oracle.layer_prefill_rows(xin, gl.w_np, cfg, rows)
-        got = np.stack([to_np(y[s, r]) for s, r in rows])
-        m = assert_bf16_parity(got, ref, f"layer {layer} (teacher-forced, rows {rows})")
+        if layer in (0, wl.layers - 1):
+            check_prefill_stages_full(gl, xin, y, kc, vc, ws, f"stack layer {layer}")
+        ref = oracle_layer_prefill_parallel(xin, gl.w_np, cfg)
+        m = assert_bf16_parity(to_np(y), ref["y"], f"layer {layer} y, every element (teacher-forced)")
         worst = m if worst is None or m["mean_rel"] > worst["mean_rel"] else worst
         cur = y
-        del gl
+        del gl, ref
     gain = si.final_norm_gain(cfg, seed=wl.seed)
     gd = to_dev(gain, cfg)
     out = torch.empty_like(cur)
     nat.rmsnorm(cur, gd, out, cfg.rms_norm_eps)
     torch.cuda.synchronize()
     assert_rounded(to_np(out), oracle.rmsnorm(to_np(cur), gain, cfg.rms_norm_eps), "final norm (teacher-forced)")
-    log(f"  worst layer mean_rel {worst['mean_rel']:.3g}, max_abs {worst['max_abs']:.3g}")
+    log(f"  worst layer mean_rel {worst['mean_rel']:.3g}, max_abs {worst['max_abs']:.3g} "
+        f"(bar {worst['max_abs_bar']:.3g})")
 
 
 def run_stack(cfg, x, layers, seed, gain):

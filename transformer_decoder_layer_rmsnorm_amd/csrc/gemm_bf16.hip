@@ -8,16 +8,13 @@
 //
 // Large tiles (256 x 256 on 8 waves, one workgroup per CU, two waves per SIMD) stage operands
 // with direct global->LDS loads (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the
-// wave's LDS base + 16 l, without passing through VGPRs), BK = 32 per stage and four stages in
-// flight, so a k-slab is requested three stages before it is used.  LDS rows are unpadded 64-byte
-// rows whose four 16-byte chunks are XOR-swizzled by row, which keeps fragment reads free of bank
-// conflicts; each load instruction covers 16 rows of one operand.  Whenever K is a multiple of 64
-// a ping-pong variant of the same tile is used instead: 64-k stages with 128-byte LDS rows (every
-// load moves whole cache lines) and the two wave groups of each SIMD alternating between memory
-// and matrix phases (see gemm_bf16_pp_kernel).  The ping-pong kernel also has a 256 x 128 form,
-// used by the fused QKV projection when 256 x 256 tiles would leave too many CUs idle.  Its
-// epilogues that read a residual stage the tile through LDS and move 16 bytes per lane (see
-// pp_store_tile).
+// wave's LDS base + 16 l, without passing through VGPRs) in 64-k stages of 128-byte LDS rows, so
+// every load moves whole cache lines, and the two wave groups of each SIMD alternate between
+// memory and matrix phases ("ping-pong", see gemm_bf16_pp_kernel).  The validated layer shapes
+// make every K a multiple of 128, so no other large-tile form is needed.  The ping-pong kernel
+// also has a 256 x 128 form, used by the fused QKV projection when 256 x 256 tiles would leave
+// too many CUs idle.  Its epilogues that read a residual stage the tile through LDS and move 16
+// bytes per lane (see pp_store_tile).
 //
 // Smaller tiles (128 x 128 on 4 waves; 64 x 64, or 64 x 128 for SwiGLU, when fewer than 256
 // tiles would remain; 64 x 128 for split-K partial slabs) keep a register prefetch: BK = 64, two LDS stages, the next k-slab fetched
@@ -411,8 +408,7 @@ __global__ __launch_bounds__(256) void gemm_qkv_qkrope_kernel(DevGemm p, QkRopeA
 }
 
 
-// ------------------------------------------------------------------ large tiles, LDS DMA
-constexpr int DBK = 32;   // k per stage: one LDS row = 64 bytes = four 16-byte chunks
+// ------------------------------------------------------------------ direct global->LDS loads
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor held in SGPRs: base, stride 0, num_records bytes (reads past them return 0).
@@ -433,135 +429,6 @@ __device__ __forceinline__ void dma16(int4v rsrc, int voff, int soff, unsigned l
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr) : "memory");
 }
-// Wait until at most N of this wave's loads are in flight, then barrier.  Also a compiler
-// memory barrier, so no LDS access moves across it.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(N) : "memory");
-}
-// Stage data landed when at most `newer` later stages (NI loads each) are still in flight.
-template <int NI, int MAXN>
-__device__ __forceinline__ void wait_stage(int newer) {
-    static_assert(MAXN <= 3 && NI * MAXN < 64, "vmcnt range");
-    if (MAXN >= 3 && newer >= 3) wait_vm_barrier<(MAXN >= 3 ? NI * 3 : 0)>();
-    else if (MAXN >= 2 && newer == 2) wait_vm_barrier<(MAXN >= 2 ? NI * 2 : 0)>();
-    else if (MAXN >= 1 && newer == 1) wait_vm_barrier<NI>();
-    else wait_vm_barrier<0>();
-}
-// Position of 16-byte chunk c of tile row `row` within the LDS row: c ^ chunk_swz(row).  Rows r,
-// r+4, r+8, r+12 (which share banks) get four distinct patterns, and rows r, r+4 differ in the
-// upper bit, so 16 lanes reading one chunk of 16 consecutive rows, or of 8 rows in two adjacent
-// chunks, touch distinct banks.
-__device__ __forceinline__ int chunk_swz(int row) { return (((row >> 2) & 1) << 1) | ((row >> 3) & 1); }
-
-template <Epilogue EPI, int BM, int BN, int WM, int WN, int S>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_dma_kernel(DevGemm p) {
-    constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
-    constexpr int NW = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 32, FN = TN / 32;
-    constexpr int IA = BM / 16 / NW, IB = BN / 16 / NW;   // load instructions per wave per stage
-    constexpr int NI = IA + IB;
-    static_assert(IA >= 1 && IB >= 1 && (BM / 16) % NW == 0 && (BN / 16) % NW == 0, "tile vs waves");
-    static_assert(!DUAL || TN % 64 == 0, "SwiGLU tiles need whole gate/up block pairs per wave");
-    static_assert(S >= 2 && S <= 5, "stages");
-    constexpr int A_ST = BM * DBK, B_ST = BN * DBK;      // elements per stage
-    __shared__ __attribute__((aligned(1024))) bf16 sA[S * A_ST];
-    __shared__ __attribute__((aligned(1024))) bf16 sB[S * B_ST];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_of(p, blockIdx.x, tm, tn);
-    const int m0 = tm * BM;
-    const int rowbytes = p.K * 2;
-
-    // Load instruction i of this wave covers tile rows (wave*IA + i)*16 .. +15 of A (resp. B);
-    // lane l moves row +l/4, LDS chunk l%4.  A rows past M read as zeros.
-    int4v ra[IA], rb[IB];
-#pragma unroll
-    for (int i = 0; i < IA; ++i) {
-        const int r0 = m0 + (wave * IA + i) * 16;
-        const int nrows = max(0, min(16, p.M - r0));
-        ra[i] = sgpr_desc(p.a + (int64_t)min(r0, p.M - 1) * p.K, nrows * rowbytes);
-    }
-#pragma unroll
-    for (int i = 0; i < IB; ++i) {
-        const int lr = (wave * IB + i) * 16;
-        const bf16* base;
-        if constexpr (DUAL) {
-            // B tile rows in blocks of 32: gate, up, gate, up, ... of output columns
-            // tn*BN/2 + 32*(row/64) + row%32
-            const int n = tn * (BN / 2) + (lr >> 6) * 32 + (lr & 31);
-            base = p.b[(lr >> 5) & 1] + (int64_t)n * p.K;
-        } else {
-            base = seg_row(p, tn * BN + lr);   // 16 rows never straddle a segment
-        }
-        rb[i] = sgpr_desc(base, 16 * rowbytes);
-    }
-    const int dma_voff = (lane >> 2) * rowbytes + (((lane & 3) ^ chunk_swz(lane >> 2)) << 4);
-    const unsigned sA_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sA;
-    const unsigned sB_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)sB;
-    auto issue = [&](int kt) {
-        const int slot = kt % S;
-        const int soff = kt * (DBK * 2);
-#pragma unroll
-        for (int i = 0; i < IA; ++i)
-            dma16(ra[i], dma_voff, soff,
-                  __builtin_amdgcn_readfirstlane(sA_lds + (slot * A_ST + (wave * IA + i) * 16 * DBK) * 2));
-#pragma unroll
-        for (int i = 0; i < IB; ++i)
-            dma16(rb[i], dma_voff, soff,
-                  __builtin_amdgcn_readfirstlane(sB_lds + (slot * B_ST + (wave * IB + i) * 16 * DBK) * 2));
-    };
-
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // fragment reads: row (wave base) + 32 i + lane%32, chunk 2 kk + lane/32 (swizzled)
-    const int fr = lane & 31;
-    const int a_rd0 = (wm * TM + fr) * DBK + (((0 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
-    const int a_rd1 = (wm * TM + fr) * DBK + (((2 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
-    const int b_rd0 = (wn * TN + fr) * DBK + (((0 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
-    const int b_rd1 = (wn * TN + fr) * DBK + (((2 + (lane >> 5)) ^ chunk_swz(fr)) << 3);
-    const int nk = p.K / DBK;
-
-#pragma unroll
-    for (int st = 0; st < S - 1; ++st)
-        if (st < nk) issue(st);
-    for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once at most min(S-2, nk-1-kt) later stages are in flight; the
-        // barrier also retires every wave's reads of slot (kt-1) % S, which is refilled next
-        wait_stage<NI, S - 2>(min(S - 2, nk - 1 - kt));
-        const bf16* pa = sA + (kt % S) * A_ST;
-        const bf16* pb = sB + (kt % S) * B_ST;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 af[FM], bfr[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(pa + (kk ? a_rd1 : a_rd0) + i * 32 * DBK);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(pb + (kk ? b_rd1 : b_rd0) + j * 32 * DBK);
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-            // the stage S-1 ahead is requested once this stage's first MFMAs are queued: right
-            // after the barrier all waves would hit the address queues at once
-            if (kk == 0 && kt + S - 1 < nk) issue(kt + S - 1);
-        }
-    }
-    write_tile<EPI, BN, TM, TN, FM, FN>(p, acc, m0, tn, wm, wn, lane);
-}
-
 
 // ------------------------------------------------------------------ large tiles: ping-pong
 // 256 x 256 tiles on 8 waves (4 x 2, each wave 64 x 128), BK = 64 per stage in two LDS stages of
@@ -1032,16 +899,6 @@ static hipError_t run_tile(DevGemm p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <Epilogue EPI, int BM, int BN, int WM, int WN, int S>
-static hipError_t run_dma_tile(DevGemm p, hipStream_t s) {
-    const int bn_out = (EPI == Epilogue::SwiGLU) ? BN / 2 : BN;
-    if (p.N % bn_out || p.K % DBK || (int64_t)p.K * 2 * 16 >= (int64_t)1 << 31) return hipErrorInvalidValue;
-    p.tiles_m = (p.M + BM - 1) / BM;
-    p.tiles_n = p.N / bn_out;
-    gemm_bf16_dma_kernel<EPI, BM, BN, WM, WN, S><<<(unsigned)(p.tiles_m * p.tiles_n), WM * WN * 64, 0, s>>>(p);
-    return hipGetLastError();
-}
-
 template <Epilogue EPI, int BN = 256>
 static hipError_t run_pp_tile(DevGemm p, hipStream_t s) {
     const int bn_out = (EPI == Epilogue::SwiGLU) ? BN / 2 : BN;
@@ -1063,12 +920,10 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     const int bn256 = DUAL ? 128 : 256, bn128 = DUAL ? 64 : 128;
     const long tiles256 = (long)((p.M + 255) / 256) * (p.N / bn256);
     const long tiles128 = (long)((p.M + 127) / 128) * (p.N / bn128);
-    // 256 x 256 tiles: the ping-pong kernel (whole-line DMA, two 64-k stages) when K allows,
-    // else the four-stage 32-k kernel.  The ping-pong kernel is also taken with one tile for only
-    // three CUs in four: its per-tile rate outweighs the idle quarter (2048 x 6144 x 1024 SwiGLU
+    // 256 x 256 tiles: the ping-pong kernel (whole-line DMA, two 64-k stages), also taken with one
+    // tile for only three CUs in four: its per-tile rate outweighs the idle quarter (2048 x 6144 x 1024 SwiGLU
     // product: 31.5 us against 38-40 us on 768 tiles of 128 x 128).
     if (tiles256 >= 192 && p.N % bn256 == 0 && p.K % 64 == 0) return run_pp_tile<EPI>(p, s);
-    if (tiles256 >= 256 && p.N % bn256 == 0) return run_dma_tile<EPI, 256, 256, 4, 2, 4>(p, s);
     if (tiles128 >= 256) return run_tile<EPI, 128, 128, 2, 2>(p, s);
     if constexpr (DUAL)
         return run_tile<EPI, 64, 128, 2, 2>(p, s);
@@ -1090,7 +945,6 @@ static int qkv_fused_kind(const GemmArgs& g, const QkRopeArgs& a) {
     const long tiles128 = (long)((g.M + 127) / 128) * (g.N / 128);
     const bool dma_ok = (int64_t)g.K * 2 * 8 < ((int64_t)1 << 31);
     if (tiles256 >= 192 && g.N % 256 == 0) return dma_ok ? 2 : 0;
-    if (tiles256 >= 256 && g.N % 256 == 0) return 0;
     if (tiles_pp128 >= 256 && dma_ok) return 3;
     return tiles128 >= 256 ? 1 : 0;
 }

@@ -168,6 +168,31 @@ qwen3_status check_sizes(const qwen3_layer* L, int32_t batch, int32_t seq_len, i
     return QWEN3_OK;
 }
 
+// Per-sequence values (first slots, padding runs) of batches above kInlinePositions sequences go
+// to the workspace through kernel arguments, kFillChunk values per launch: a host-to-device copy
+// from host memory the caller does not pin would make the host wait for it, and a captured copy
+// would read host memory that no longer exists when the graph is replayed.
+constexpr int kFillChunk = 256;
+struct I32Chunk {
+    int32_t v[kFillChunk];
+};
+__global__ __launch_bounds__(kFillChunk) void fill_i32_kernel(int32_t* __restrict__ dst, I32Chunk c, int n) {
+    const int i = threadIdx.x;
+    if (i < n) dst[i] = c.v[i];
+}
+
+hipError_t upload_i32(int32_t* dst, const std::vector<int32_t>& host, hipStream_t s) {
+    for (size_t o = 0; o < host.size(); o += kFillChunk) {
+        const int n = (int)std::min<size_t>(kFillChunk, host.size() - o);
+        I32Chunk c;
+        std::memcpy(c.v, host.data() + o, sizeof(int32_t) * n);
+        fill_i32_kernel<<<1, kFillChunk, 0, s>>>(dst + o, c, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // ------------------------------------------------------------------ profiling helpers
 hipEvent_t take_event(qwen3_layer* L) {
     if (!L->free_events.empty()) {
@@ -496,9 +521,8 @@ qwen3_status prefill_impl(qwen3_layer* L, const void* x, void* y, int32_t batch,
             host[batch + b] = host[b];
             host[2 * batch + b] = pad_lens ? pad_lens[b] : 0;
         }
-        const hipError_t e = hipMemcpyAsync(ws + lay.lens, host.data(), sizeof(int32_t) * host.size(),
-                                            hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying start positions: %s", hipGetErrorString(e));
+        const hipError_t e = upload_i32(reinterpret_cast<int32_t*>(ws + lay.lens), host, s);
+        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "uploading start positions: %s", hipGetErrorString(e));
         pos.dev = reinterpret_cast<const int32_t*>(ws + lay.lens);
         if (any_pad) {
             pos.dev_pad = pos.dev + batch;
@@ -613,9 +637,8 @@ qwen3_status decode_impl(qwen3_layer* L, const void* x, void* y, int32_t batch, 
             host[batch + b] = any_pad ? pad_starts[b] : 0;
             host[2 * batch + b] = any_pad ? pad_lens[b] : 0;
         }
-        const hipError_t e = hipMemcpyAsync(ws + lay.lens, host.data(), sizeof(int32_t) * host.size(),
-                                            hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "copying cache_lens: %s", hipGetErrorString(e));
+        const hipError_t e = upload_i32(reinterpret_cast<int32_t*>(ws + lay.lens), host, s);
+        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "uploading cache_lens: %s", hipGetErrorString(e));
         pos.dev = reinterpret_cast<const int32_t*>(ws + lay.lens);
         if (any_pad) {
             pos.dev_pad = pos.dev + batch;

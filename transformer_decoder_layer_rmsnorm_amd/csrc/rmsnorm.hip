@@ -6,8 +6,8 @@
 // before the gain; the difference is below one output ulp).  Zero-centred gains (the page's
 // parity detail 2: Gemma and the Qwen3.5 family store g and apply 1 + g) take goff = 1.
 //
-// Memory-bound: each row is read once (16-byte loads, kept in registers up to 4096 wide) and
-// written once.  Four rows per 256-thread workgroup.
+// Memory-bound: each row is read once (16-byte loads, kept in registers up to 4096 wide; wider
+// rows are read twice) and written once.  Four rows per 256-thread workgroup.
 //
 // Split-K residual form: when o_proj's K range is split across workgroups, its fp32 partial
 // slabs are summed here, in a fixed order (deterministic), together with the residual:
@@ -78,12 +78,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
     }
 }
 
-// Input RMSNorm (bf16, width <= 4096) plus the RoPE table row of each token: lane i of the
-// row's wave forms the angle of frequency i (see RopeTable).
+// Input RMSNorm (bf16) plus the RoPE table row of each token: lane i of the row's wave forms the
+// angle of frequency i (see RopeTable).  Rows up to 4096 wide stay in registers between the
+// reduction and the output; wider rows (WIDE) are read twice.
+template <bool WIDE>
 __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restrict__ x, const bf16* __restrict__ g,
                                                            bf16* __restrict__ y, int64_t rows, int width, float eps,
                                                            float goff, RopeTable rope) {
-    constexpr int MAXC = 8;
+    constexpr int MAXC = WIDE ? 1 : 8;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -92,13 +94,21 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
     const int nchunk = width >> 3;
     float v[MAXC][8];
     float ss = 0.f;
+    if constexpr (WIDE) {
+        for (int c = lane; c < nchunk; c += kWave) {
+            load8(xr + c * 8, v[0]);
 #pragma unroll
-    for (int j = 0; j < MAXC; ++j) {
-        const int c = lane + j * kWave;
-        if (c < nchunk) {
-            load8(xr + c * 8, v[j]);
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[0][i], v[0][i], ss);
+        }
+    } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = lane + j * kWave;
+            if (c < nchunk) {
+                load8(xr + c * 8, v[j]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+            }
         }
     }
     // the angle of frequency `lane` at this token's position, while the loads are in flight
@@ -112,15 +122,26 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
     reinterpret_cast<float2*>(rope.cs)[row * 64 + lane] = cs;
     if (lane == 0) rope.slot[row] = lin;
     const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
-#pragma unroll
-    for (int j = 0; j < MAXC; ++j) {
-        const int c = lane + j * kWave;
-        if (c < nchunk) {
+    if constexpr (WIDE) {
+        for (int c = lane; c < nchunk; c += kWave) {
             float gv[8], o[8];
+            load8(xr + c * 8, v[0]);
             load8(g + c * 8, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[0][i] * rstd);
             store8(yr + c * 8, o);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = lane + j * kWave;
+            if (c < nchunk) {
+                float gv[8], o[8];
+                load8(g + c * 8, gv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+                store8(yr + c * 8, o);
+            }
         }
     }
 }
@@ -128,9 +149,14 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
 hipError_t launch_rmsnorm_rope(const void* x, const void* g, void* y, int64_t rows, int width, float eps, float goff,
                                const RopeTable& rope, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if ((width & 7) || width > 8 * 8 * kWave || rope.T <= 0 || !rope.cs || !rope.slot) return hipErrorInvalidValue;
-    rmsnorm_rope_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g),
-                                                                   static_cast<bf16*>(y), rows, width, eps, goff, rope);
+    if ((width & 7) || rope.T <= 0 || !rope.cs || !rope.slot) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    if (width <= 8 * 8 * kWave)
+        rmsnorm_rope_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g),
+                                                        static_cast<bf16*>(y), rows, width, eps, goff, rope);
+    else
+        rmsnorm_rope_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g),
+                                                       static_cast<bf16*>(y), rows, width, eps, goff, rope);
     return hipGetLastError();
 }
 
@@ -148,7 +174,22 @@ static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t ro
 }
 
 
-template <typename TX, typename TY>
+// x + the split-K slabs of one 8-element chunk, summed in a fixed order (deterministic)
+template <typename TX>
+__device__ __forceinline__ void resid_chunk(const TX* x, const float* part, int splits, int64_t slab, int64_t o,
+                                            float* v) {
+    load8(x + o, v);
+    for (int sp = 0; sp < splits; ++sp) {
+        float pv[8];
+        load8(part + sp * slab + o, pv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += pv[i];
+    }
+}
+
+// Rows up to 4096 wide keep x1 in registers between the reduction and the output; wider rows
+// (WIDE) form x1 again in the output pass (same operands, same order, same value).
+template <typename TX, typename TY, bool WIDE>
 __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restrict__ x, const float* __restrict__ part,
                                                                int splits, float* __restrict__ x1,
                                                                const TY* __restrict__ g, TY* __restrict__ y,
@@ -160,34 +201,47 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
     const int64_t off = row * width;
     const int64_t slab = rows * width;
     const int nchunk = width >> 3;
-    float v[MAXC][8];
     float ss = 0.f;
+    if constexpr (WIDE) {
+        for (int c = lane; c < nchunk; c += kWave) {
+            float v[8];
+            resid_chunk(x, part, splits, slab, off + c * 8, v);
+            store8(x1 + off + c * 8, v);
 #pragma unroll
-    for (int j = 0; j < MAXC; ++j) {
-        const int c = lane + j * kWave;
-        if (c < nchunk) {
-            load8(x + off + c * 8, v[j]);
-            for (int sp = 0; sp < splits; ++sp) {
-                float pv[8];
-                load8(part + sp * slab + off + c * 8, pv);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[j][i] += pv[i];
-            }
-            store8(x1 + off + c * 8, v[j]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
         }
-    }
-    const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
-#pragma unroll
-    for (int j = 0; j < MAXC; ++j) {
-        const int c = lane + j * kWave;
-        if (c < nchunk) {
-            float gv[8], o[8];
+        const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
+        for (int c = lane; c < nchunk; c += kWave) {
+            float v[8], gv[8], o[8];
+            resid_chunk(x, part, splits, slab, off + c * 8, v);
             load8(g + c * 8, gv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+            for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[i] * rstd);
             store8(y + off + c * 8, o);
+        }
+    } else {
+        float v[MAXC][8];
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = lane + j * kWave;
+            if (c < nchunk) {
+                resid_chunk(x, part, splits, slab, off + c * 8, v[j]);
+                store8(x1 + off + c * 8, v[j]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
+            }
+        }
+        const float rstd = rsqrtf(wave_sum(ss) / (float)width + eps);
+#pragma unroll
+        for (int j = 0; j < MAXC; ++j) {
+            const int c = lane + j * kWave;
+            if (c < nchunk) {
+                float gv[8], o[8];
+                load8(g + c * 8, gv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
+                store8(y + off + c * 8, o);
+            }
         }
     }
 }
@@ -195,18 +249,21 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(const TX* __restr
 hipError_t launch_residual_rmsnorm(const void* x, DType xt, const float* part, int splits, float* x1, const void* g,
                                    void* y, DType yt, int64_t rows, int width, float eps, float goff, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if ((width & 7) || width > 8 * 8 * kWave || splits < 1) return hipErrorInvalidValue;
+    if ((width & 7) || splits < 1) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((rows + 3) / 4));
-    if (xt == DType::BF16 && yt == DType::BF16)
-        residual_rmsnorm_kernel<bf16, bf16><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), part, splits, x1,
-                                                                  static_cast<const bf16*>(g), static_cast<bf16*>(y),
-                                                                  rows, width, eps, goff);
-    else if (xt == DType::F32 && yt == DType::F32)
-        residual_rmsnorm_kernel<float, float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), part, splits, x1,
-                                                                    static_cast<const float*>(g), static_cast<float*>(y),
-                                                                    rows, width, eps, goff);
-    else
+    const bool wide = width > 8 * 8 * kWave;
+#define Q3_RESID_RMS(TX, TY, W)                                                                                   \
+    residual_rmsnorm_kernel<TX, TY, W><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), part, splits, x1,         \
+                                                             static_cast<const TY*>(g), static_cast<TY*>(y), rows, \
+                                                             width, eps, goff)
+    if (xt == DType::BF16 && yt == DType::BF16) {
+        if (wide) Q3_RESID_RMS(bf16, bf16, true); else Q3_RESID_RMS(bf16, bf16, false);
+    } else if (xt == DType::F32 && yt == DType::F32) {
+        if (wide) Q3_RESID_RMS(float, float, true); else Q3_RESID_RMS(float, float, false);
+    } else {
         return hipErrorInvalidValue;
+    }
+#undef Q3_RESID_RMS
     return hipGetLastError();
 }
 
