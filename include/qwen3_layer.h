@@ -130,7 +130,9 @@ void qwen3_layer_destroy(qwen3_layer* layer);
 
 /* Workspace bytes for a prefill of [batch, seq_len] tokens (also onto a
  * non-empty cache) and for a decode of `batch` tokens over caches of
- * `cache_capacity` slots (pass seq_len = 1 for decode only).  Host only. */
+ * `cache_capacity` slots (pass seq_len = 1 for decode only).  Host only.
+ * cache_capacity is an argument because the decode attention's per-split
+ * partial results grow with the cache length it may have to cover. */
 qwen3_status qwen3_layer_workspace_size(const qwen3_layer* layer, int32_t batch, int32_t seq_len,
                                         int32_t cache_capacity, size_t* bytes);
 
@@ -161,9 +163,10 @@ qwen3_status qwen3_layer_prefill(qwen3_layer* layer, const void* x, void* y, int
  * diffusion, lesson 6", section 8: a shared prefix's keys and values are
  * computed once and reused).  Running a prompt as prefill(T1) followed by
  * prefill_at(T2, start T1) gives the rows of prefill(T1 + T2).  Up to 64
- * sequences the start positions travel as launch arguments; for more, they
- * are copied into the workspace (which must then also cover the `lens` region
- * of qwen3_layer_workspace_layout).  y may alias x.
+ * sequences the start positions travel as launch arguments; for more, small
+ * kernels whose launch arguments carry them (256 values each) write them into
+ * the workspace (which must then also cover the `lens` region of
+ * qwen3_layer_workspace_layout), with no host-to-device copy.  y may alias x.
  * Errors: INVALID_ARGUMENT, OUT_OF_RANGE (start_positions[b] < 0,
  * start_positions[b] + seq_len > cache_capacity or > max_position_embeddings),
  * WORKSPACE_TOO_SMALL, DEVICE. */
@@ -186,7 +189,8 @@ qwen3_status qwen3_layer_prefill_at(qwen3_layer* layer, const void* x, void* y, 
  * max(start_b - 1, 0) when it is padding; its cache slot is start_b + t either
  * way.  Later decode steps pass the same run to qwen3_layer_decode_padded.
  * Up to 64 sequences the per-sequence values travel as launch arguments; for
- * more they are copied into the workspace's `lens` region.
+ * more they are written into the workspace's `lens` region by small kernels
+ * whose launch arguments carry them (no host-to-device copy).
  * Errors: as qwen3_layer_prefill_at, plus OUT_OF_RANGE for pad_lens[b] < 0 or
  * pad_lens[b] > seq_len. */
 qwen3_status qwen3_layer_prefill_padded(qwen3_layer* layer, const void* x, void* y, int32_t batch,
@@ -201,8 +205,9 @@ qwen3_status qwen3_layer_prefill_padded(qwen3_layer* layer, const void* x, void*
  * cache_lens[b], its khat / v are written to that slot and it attends keys
  * 0..cache_lens[b] of its own sequence.  cache_lens is not modified (the caller
  * advances it).  y may alias x.  Up to 64 sequences the lengths travel to the
- * kernels as launch arguments; for more, they are copied into the workspace
- * with hipMemcpyAsync.  Either way the host array may be reused once the call
+ * kernels as launch arguments; for more, small kernels whose launch arguments
+ * carry them (256 values each) write them into the workspace, with no
+ * host-to-device copy.  Either way the host array may be reused once the call
  * returns.
  * Errors: INVALID_ARGUMENT, OUT_OF_RANGE (cache_lens[b] < 0,
  * cache_lens[b] >= cache_capacity, cache_lens[b] >= max_position_embeddings),
