@@ -274,6 +274,27 @@ qwen3_status qwen3_layer_decode_window(qwen3_layer* layer, const void* x, void* 
                                        int32_t cache_capacity, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory or
+ * call hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The same computation, kernels and errors as
+ * qwen3_layer_decode, but the intermediates live in a static device array of
+ * the library (32 MiB; each GPU the library runs on holds its own copy until
+ * the process ends) instead of a caller workspace.  The call allocates nothing:
+ * no hipMalloc / hipFree, no profiling events (qwen3_layer_set_profiling has no
+ * effect on it).  Its first call on a device looks the array up on that device
+ * (hipGetSymbolAddress), so it must run with `stream`'s device current.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (several streams or threads at once) race and must not be issued; calls in
+ * order on one stream are fine.  Nothing in the array needs clearing between
+ * calls (every value a call reads was written earlier in the same call).
+ * Errors: as qwen3_layer_decode; WORKSPACE_TOO_SMALL when the decode of `batch`
+ * sequences over `cache_capacity` slots needs more than the 32 MiB (the sizes
+ * qwen3_layer_workspace_size reports for the same call); INVALID_ARGUMENT when
+ * the stream belongs to another device than the current one. */
+qwen3_status qwen3_layer_decode_noalloc(qwen3_layer* layer, const void* x, void* y, int32_t batch,
+                                        const int32_t* cache_lens, void* k_cache, void* v_cache,
+                                        int32_t cache_capacity, void* stream);
+
 /* RMSNorm of `rows` rows of `width` elements ("17. A modern architecture:
  * Qwen3", section RMSNorm): y = weight * x / sqrt(mean(x^2) + eps), reduced in
  * fp32.  x, weight and y all hold `dtype`; used for the final norm after a

@@ -281,3 +281,19 @@ def test_python_binding_raises_with_message():
     with pytest.raises(nat.Qwen3Error) as e:
         nat.check(nat.QWEN3_ERR_OUT_OF_RANGE, "probe")
     assert e.value.status == nat.QWEN3_ERR_OUT_OF_RANGE
+
+
+def test_decode_noalloc_rejects_before_any_device_call(layer):
+    """The allocation-free decode validates on the host first: a decode too large for its
+    32 MiB scratch array, bad lengths and NULL pointers are refused before the array is looked
+    up on a device (there is none here)."""
+    L = nat.lib()
+    lens = (ctypes.c_int32 * 64)(*([32768] * 64))
+    st = L.qwen3_layer_decode_noalloc(layer, FAKE, FAKE, 64, lens, FAKE, FAKE, 32769, None)
+    assert st == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL, err()
+    assert "32 MiB" in err() or "bytes of scratch" in err()
+    one = (ctypes.c_int32 * 1)(5)
+    assert L.qwen3_layer_decode_noalloc(layer, None, FAKE, 1, one, FAKE, FAKE, 16, None) == \
+        nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert L.qwen3_layer_decode_noalloc(layer, FAKE, FAKE, 0, one, FAKE, FAKE, 16, None) == \
+        nat.QWEN3_ERR_INVALID_ARGUMENT

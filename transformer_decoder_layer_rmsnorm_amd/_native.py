@@ -27,7 +27,7 @@ EXPORTED = (
     "qwen3_layer_create", "qwen3_layer_destroy", "qwen3_layer_workspace_size",
     "qwen3_layer_workspace_layout", "qwen3_layer_prefill", "qwen3_layer_prefill_at",
     "qwen3_layer_prefill_padded", "qwen3_layer_prefill_window", "qwen3_layer_decode",
-    "qwen3_layer_decode_padded", "qwen3_layer_decode_window",
+    "qwen3_layer_decode_padded", "qwen3_layer_decode_window", "qwen3_layer_decode_noalloc",
     "qwen3_rmsnorm", "qwen3_rmsnorm_gain_offset", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
     "qwen3_status_string", "qwen3_last_error",
 )
@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
         "qwen3_layer_decode": ([P, P, P, I32, ctypes.POINTER(I32), P, P, I32, P, SZ, P], ctypes.c_int),
         "qwen3_layer_decode_padded": ([P, P, P, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
                                        P, P, I32, P, SZ, P], ctypes.c_int),
+        "qwen3_layer_decode_noalloc": ([P, P, P, I32, ctypes.POINTER(I32), P, P, I32, P], ctypes.c_int),
         "qwen3_rmsnorm": ([P, P, P, I64, I32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_rmsnorm_gain_offset": ([P, P, P, I64, I32, F32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_layer_set_profiling": ([P, I32], ctypes.c_int),
@@ -215,6 +216,14 @@ class Layer:
         check(lib().qwen3_layer_decode(self._h, _ptr(x), _ptr(y), b, lens, _ptr(k_cache), _ptr(v_cache),
                                        k_cache.shape[2], _ptr(workspace), nbytes, _stream(stream)),
               "qwen3_layer_decode")
+
+    def decode_noalloc(self, x, y, cache_lens, k_cache, v_cache, stream=None) -> None:
+        """One token per sequence with the intermediates in the library's static device array
+        (qwen3_layer_decode_noalloc): no workspace, nothing allocated."""
+        b = x.shape[0]
+        lens = (ctypes.c_int32 * b)(*[int(v) for v in cache_lens])
+        check(lib().qwen3_layer_decode_noalloc(self._h, _ptr(x), _ptr(y), b, lens, _ptr(k_cache), _ptr(v_cache),
+                                               k_cache.shape[2], _stream(stream)), "qwen3_layer_decode_noalloc")
 
     def prefill_window(self, x, y, k_cache, v_cache, workspace, window, sinks=0, start_positions=None,
                        stream=None) -> None:

@@ -213,9 +213,9 @@ int stage_id(qwen3_layer* L, const char* name) {
 }
 
 template <typename F>
-qwen3_status run_stage(qwen3_layer* L, const char* name, hipStream_t s, F&& launch) {
+qwen3_status run_stage(qwen3_layer* L, bool prof, const char* name, hipStream_t s, F&& launch) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (L->profiling) {
+    if (prof) {
         std::lock_guard<std::mutex> g(L->prof_mu);
         e0 = take_event(L);
         e1 = take_event(L);
@@ -223,7 +223,7 @@ qwen3_status run_stage(qwen3_layer* L, const char* name, hipStream_t s, F&& laun
     }
     const hipError_t err = launch();
     if (err != hipSuccess) return fail(QWEN3_ERR_DEVICE, "%s: %s", name, hipGetErrorString(err));
-    if (L->profiling && e0 && e1) {
+    if (prof && e0 && e1) {
         std::lock_guard<std::mutex> g(L->prof_mu);
         hipEventRecord(e1, s);
         L->pending.push_back({stage_id(L, name), e0, e1});
@@ -252,7 +252,7 @@ GemmArgs gemm(const void* a, std::initializer_list<const void*> b, std::initiali
 // The whole layer on M = B*T tokens.  `pos` gives the position of token 0 of each sequence.
 qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, void* kc, void* vc, int cap,
                        char* ws, const Layout& lay, const SeqPositions& pos, const LocalAttn& local, bool decode,
-                       hipStream_t s) {
+                       hipStream_t s, bool allow_profiling = true) {
     const qwen3_config& c = L->cfg;
     const DType t = dt(c);
     const int M = B * T, H = c.hidden_size, D = c.head_dim, I = c.intermediate_size;
@@ -272,8 +272,9 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
         return g.M <= 64 ? launch_gemv_bf16(g, s) : launch_gemm_bf16(g, s);
     };
     qwen3_status st;
+    const bool prof = allow_profiling && L->profiling;
 #define STAGE(name, expr)                                    \
-    if ((st = run_stage(L, name, s, [&]() { return (expr); })) != QWEN3_OK) return st;
+    if ((st = run_stage(L, prof, name, s, [&]() { return (expr); })) != QWEN3_OK) return st;
 
     QkRopeArgs qa{};
     qa.qkv = qkv;
@@ -587,7 +588,7 @@ namespace {
 qwen3_status decode_impl(qwen3_layer* L, const void* x, void* y, int32_t batch, const int32_t* cache_lens,
                          const int32_t* pad_starts, const int32_t* pad_lens, const LocalAttn& local, void* k_cache,
                          void* v_cache, int32_t cache_capacity, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         void* stream, bool allow_profiling = true) {
     qwen3_status st = check_sizes(L, batch, 1, cache_capacity);
     if (st != QWEN3_OK) return st;
     if (!x || !y || !k_cache || !v_cache || !workspace || !cache_lens)
@@ -645,7 +646,46 @@ qwen3_status decode_impl(qwen3_layer* L, const void* x, void* y, int32_t batch, 
             pos.n_pad_inline = batch;
         }
     }
-    return run_layer(L, x, y, batch, 1, k_cache, v_cache, cache_capacity, ws, lay, pos, local, true, s);
+    return run_layer(L, x, y, batch, 1, k_cache, v_cache, cache_capacity, ws, lay, pos, local, true, s,
+                     allow_profiling);
+}
+
+// ------------------------------------------------------------------ allocation-free decode
+// For callers that cannot allocate (code under stream capture, tight serving loops): the decode
+// intermediates live in this file-scope device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy from module load until the process ends.  In host code
+// `scratch` only names the symbol: its device address comes from hipGetSymbolAddress, taken once
+// per device (with that device current) and kept below.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+qwen3_status scratch_of_current_device(hipStream_t s, char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(QWEN3_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    if (s) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(s, &sdev);
+        if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(QWEN3_ERR_INVALID_ARGUMENT, "the stream belongs to device %d, the current device is %d",
+                        (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(QWEN3_ERR_DEVICE, "locating the scratch array on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<char*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return QWEN3_OK;
 }
 
 }  // namespace
@@ -682,6 +722,27 @@ qwen3_status qwen3_layer_decode(qwen3_layer* L, const void* x, void* y, int32_t 
                                 size_t workspace_bytes, void* stream) {
     return decode_impl(L, x, y, batch, cache_lens, nullptr, nullptr, LocalAttn{0, 0, 0}, k_cache, v_cache,
                        cache_capacity, workspace, workspace_bytes, stream);
+}
+
+qwen3_status qwen3_layer_decode_noalloc(qwen3_layer* L, const void* x, void* y, int32_t batch,
+                                        const int32_t* cache_lens, void* k_cache, void* v_cache,
+                                        int32_t cache_capacity, void* stream) {
+    qwen3_status st = check_sizes(L, batch, 1, cache_capacity);
+    if (st != QWEN3_OK) return st;
+    const size_t need = make_layout(L->cfg, batch, 1, cache_capacity).total;
+    if (need > kScratchBytes)
+        return fail(QWEN3_ERR_WORKSPACE_TOO_SMALL,
+                    "a decode of %d sequences over %d cache slots needs %zu bytes of scratch; the allocation-free "
+                    "entry point holds %zu",
+                    batch, cache_capacity, need, kScratchBytes);
+    if (!x || !y || !k_cache || !v_cache || !cache_lens)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "x, y, cache_lens, k_cache and v_cache must be non-NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = nullptr;
+    if ((st = scratch_of_current_device(s, &ws)) != QWEN3_OK) return st;
+    // no profiling events here even when profiling is on: creating them allocates
+    return decode_impl(L, x, y, batch, cache_lens, nullptr, nullptr, LocalAttn{0, 0, 0}, k_cache, v_cache,
+                       cache_capacity, ws, kScratchBytes, stream, false);
 }
 
 qwen3_status qwen3_rmsnorm(const void* x, const void* weight, void* y, int64_t rows, int32_t width, float eps,
