@@ -37,6 +37,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 METRIC = "Qwen3-layer prefill tokens/s & % MFMA peak; 32K decode attn % HBM BW"
 CU_COUNT = 256
+XCD_COUNT = 8
 
 SHORT = {"c1": "tiny-f32-layer", "c2": "qwen3-0.6b-layer-prefill", "c3": "qwen3-0.6b-stack28-prefill",
          "c4": "qwen3-8b-layer-prefill", "c5": "qwen3-8b-layer-decode-32k"}
@@ -335,7 +336,7 @@ def bench_decode(torch, si, nat, wl, steps, warmup, w_np=None):
             "roofline": {"bound": "hbm", "kernel": "attention_decode_split + attention_decode_combine",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": measured_traffic("attention_decode_split", wl.name),
+                         "traffic": measured_traffic("attention_decode_split + attention_decode_combine", wl.name),
                          "avg_ms": round(attn_ms, 5), "bytes_per_launch": kv,
                          "split_kernel_only": {"avg_ms": round(avg["attention_decode_split"], 5),
                                                "achieved": round(split_gbs, 1),
@@ -482,24 +483,101 @@ def decode_parity_inputs(torch, si, nat, wl, w_np, nseq=2):
 
 def _short(name):
     import re
+    if name.startswith("_Z"):
+        import subprocess
+        try:
+            name = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip() or name
+        except OSError:
+            pass
     name = re.sub(r"\(anonymous namespace\)::|q3::", "", name)
+    name = name.replace("bool _Accum", "bf16").replace("__bf16", "bf16")
     return re.sub(r"^void ", "", name)
+
+
+def _ours(name):
+    """Kernels of this library (torch's setup kernels and runtime copies are left out)."""
+    return not (name.startswith("at::") or name.startswith("void at::") or "rocclr" in name)
+
+
+# Copy calibration of the byte counters (a plain 256 MiB device copy in the same runs):
+# FETCH_SIZE reads half the bytes read, WRITE_SIZE the bytes written.
+FETCH_FACTOR = 2.0
+WRITE_FACTOR = 1.0
+# The dominant kernel of each workload's step, as the rocprofv3 database names it: (kernel name
+# prefix, grid in workgroups) -> (stage, workload, source file).
+ROOFLINE_KERNELS = {
+    ("gemm_bf16_pp_kernel<(Epilogue)2, 256>", (3072, 1, 1)): ("gemm_gate_up_swiglu", "qwen3-8b-layer-prefill",
+                                                            "transformer_decoder_layer_rmsnorm_amd/csrc/gemm_bf16.hip"),
+    ("flash_prefill_kernel<2, 2, false>", (512, 1, 1)): ("attention", "qwen3-0.6b-layer-prefill",
+                                                        "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
+    ("flash_prefill_kernel<2, 1, false>", (2048, 1, 1)): ("attention", "qwen3-0.6b-stack28-prefill",
+                                                         "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
+    ("flash_prefill_kernel<4, 1, false>", (2048, 1, 1)): ("attention", "qwen3-8b-layer-prefill",
+                                                         "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
+}
+DECODE_KERNELS = (("decode_split_kernel<4>", (65, 8, 16)), ("decode_combine_kernel", (32, 16, 1)))
+
+
+def _traffic(dbs, mode):
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) from the databases of the two
+    counter runs, and the calibrated HBM bytes per dispatch."""
+    import collections
+    import hashlib
+    import sqlite3
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for db in dbs:
+        c = sqlite3.connect(db).cursor()
+        for n, gx, gy, gz, wx, cn, v in c.execute(
+                "select kernel_name, grid_size_x, grid_size_y, grid_size_z, workgroup_size_x, counter_name, value "
+                "from counters_collection").fetchall():
+            if _ours(n) and cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                agg[(_short(n), (gx // max(wx, 1), gy, gz))][cn].append(v)
+    avg = lambda v: sum(v) / len(v) if v else float("nan")
+    byts = lambda a: 1024 * (FETCH_FACTOR * avg(a["FETCH_SIZE"]) + WRITE_FACTOR * avg(a["WRITE_SIZE"]))
+    if mode == "traffic":
+        lines = ["| kernel | grid (workgroups) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes |",
+                 "|---|---|---|---|---|---|"]
+        for k in sorted(agg, key=lambda k: -avg(agg[k]["FETCH_SIZE"])):
+            a = agg[k]
+            lines.append(f"| `{k[0]}` | {k[1]} | {len(a['FETCH_SIZE'])} | {avg(a['FETCH_SIZE']):.1f} | "
+                         f"{avg(a['WRITE_SIZE']):.1f} | {byts(a):.4g} |")
+        return "\n".join(lines)
+    here = os.path.dirname(os.path.abspath(__file__))
+    sha = lambda p: hashlib.sha256(open(os.path.join(here, p), "rb").read()).hexdigest()
+    entries = []
+    for (prefix, grid), (stage, wl, source) in ROOFLINE_KERNELS.items():
+        for (name, g), a in agg.items():
+            if name.startswith(prefix) and g == grid:
+                entries.append({"kernel": stage, "workload": wl, "grid": list(grid),
+                                "fetch_kib": round(avg(a["FETCH_SIZE"]), 1), "write_kib": round(avg(a["WRITE_SIZE"]), 1),
+                                "traffic_bytes": int(byts(a)), "source": source, "source_sha256": sha(source)})
+    dec = [a for (name, g), a in agg.items() for p, gg in DECODE_KERNELS if name.startswith(p) and g == gg]
+    if len(dec) == 2:
+        src = "transformer_decoder_layer_rmsnorm_amd/csrc/attention_decode.hip"
+        entries.append({"kernel": "attention_decode_split + attention_decode_combine",
+                        "workload": "qwen3-8b-layer-decode-32k", "grid": [list(g) for _, g in DECODE_KERNELS],
+                        "traffic_bytes": int(sum(byts(a) for a in dec)), "source": src, "source_sha256": sha(src)})
+    return json.dumps({"fetch_factor": FETCH_FACTOR, "write_factor": WRITE_FACTOR, "entries": entries}, indent=1)
 
 
 def summarize_rocprof(db, mode):
     """Markdown table from a rocprofv3 database of this benchmark: 'trace' (durations per
     kernel and grid), 'traffic' (FETCH_SIZE / WRITE_SIZE per dispatch), or 'mfma' (MFMA
-    utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (4 * CUs * GRBM_GUI_ACTIVE), and the clock
-    GRBM_GUI_ACTIVE / duration)."""
+    utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs * 256 CUs * one XCD's GRBM_GUI_ACTIVE), the
+    share of SIMD cycles whose matrix pipe was busy, and the clock = one XCD's GRBM_GUI_ACTIVE /
+    the dispatch's duration, meaningful for dispatches far longer than the counter overhead)."""
     import collections
     import sqlite3
+    if mode in ("traffic", "traffic-json"):
+        return _traffic(db.split(","), mode)
     c = sqlite3.connect(db).cursor()
     lines = []
     if mode == "trace":
         rows = c.execute("select name, grid_x, grid_y, grid_z, workgroup_x, start, end from kernels").fetchall()
         agg = collections.defaultdict(list)
         for n, gx, gy, gz, wx, s, e in rows:
-            agg[(_short(n), gx // max(wx, 1), gy, gz)].append((e - s) / 1e3)
+            if _ours(n):
+                agg[(_short(n), gx // max(wx, 1), gy, gz)].append((e - s) / 1e3)
         lines.append("| kernel | grid (workgroups) | calls | avg us | median us |")
         lines.append("|---|---|---|---|---|")
         for (n, gx, gy, gz), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
@@ -507,45 +585,35 @@ def summarize_rocprof(db, mode):
             lines.append(f"| `{n}` | ({gx}, {gy}, {gz}) | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} |")
         return "\n".join(lines)
     rows = c.execute("select dispatch_id, kernel_name, grid_size_x, grid_size_y, grid_size_z, workgroup_size_x, "
-                     "counter_name, value from counters_collection").fetchall()
+                     "counter_name, value, duration from counters_collection").fetchall()
     disp = collections.defaultdict(lambda: collections.defaultdict(float))
-    key = {}
-    for di, n, gx, gy, gz, wx, cn, v in rows:
+    key, dur = {}, {}
+    for di, n, gx, gy, gz, wx, cn, v, du in rows:
+        if not _ours(n):
+            continue
         disp[di][cn] += v
         key[di] = (_short(n), gx // max(wx, 1), gy, gz)
-    dur = {}
-    try:
-        for di, s, e in c.execute("select dispatch_id, start, end from kernels").fetchall():
-            dur[di] = (e - s)
-    except sqlite3.Error:
-        pass
+        dur[di] = du
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     for di, cs in disp.items():
         for cn, v in cs.items():
             agg[key[di]][cn].append(v)
-        if di in dur and "GRBM_GUI_ACTIVE" in cs and dur[di] > 0:
-            agg[key[di]]["_mhz"].append(cs["GRBM_GUI_ACTIVE"] / dur[di] * 1e3)
+        if dur.get(di, 0) > 0:
             agg[key[di]]["_us"].append(dur[di] / 1e3)
+            if "GRBM_GUI_ACTIVE" in cs:
+                # the database sums GRBM_GUI_ACTIVE over the 8 XCDs; one XCD's count is the
+                # kernel's busy cycles (rocprofv3's derived metrics take the max over XCDs)
+                agg[key[di]]["_mhz"].append(cs["GRBM_GUI_ACTIVE"] / XCD_COUNT / dur[di] * 1e3)
     avg = lambda v: sum(v) / len(v) if v else float("nan")
-    if mode == "traffic":
-        lines.append("| kernel | grid (workgroups) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB |")
-        lines.append("|---|---|---|---|---|")
-        for k in sorted(agg, key=lambda k: -avg(agg[k].get("FETCH_SIZE", [0]))):
-            a = agg[k]
-            n = max(len(a.get("FETCH_SIZE", [])), len(a.get("WRITE_SIZE", [])))
-            lines.append(f"| `{k[0]}` | {k[1:]} | {n} | {avg(a.get('FETCH_SIZE', [])):.1f} | "
-                         f"{avg(a.get('WRITE_SIZE', [])):.1f} |")
-        return "\n".join(lines)
-    lines.append("| kernel | grid (workgroups) | dispatches | avg us | MFMA busy % | clock MHz | "
-                 "SQ_BUSY_CYCLES / GRBM_GUI_ACTIVE | bf16 MFMA MOPS |")
-    lines.append("|---|---|---|---|---|---|---|---|")
+    lines.append("| kernel | grid (workgroups) | dispatches | avg us | MFMA busy % | clock MHz | bf16 MFMA MOPS |")
+    lines.append("|---|---|---|---|---|---|---|")
     for k in sorted(agg, key=lambda k: -avg(agg[k].get("_us", [0])) * len(agg[k].get("_us", [0]))):
         a = agg[k]
-        gui = avg(a.get("GRBM_GUI_ACTIVE", []))
+        gui = avg(a.get("GRBM_GUI_ACTIVE", [])) / XCD_COUNT
+        # SQ_VALU_MFMA_BUSY_CYCLES is summed over the 4 * 256 SIMDs
         util = 100.0 * avg(a.get("SQ_VALU_MFMA_BUSY_CYCLES", [])) / (4 * CU_COUNT * gui) if gui else float("nan")
-        sqb = avg(a.get("SQ_BUSY_CYCLES", [])) / gui if gui else float("nan")
         lines.append(f"| `{k[0]}` | {k[1:]} | {len(a.get('GRBM_GUI_ACTIVE', []))} | {avg(a.get('_us', [])):.2f} | "
-                     f"{util:.1f} | {avg(a.get('_mhz', [])):.0f} | {sqb:.2f} | "
+                     f"{util:.1f} | {avg(a.get('_mhz', [])):.0f} | "
                      f"{avg(a.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', [])):.4g} |")
     return "\n".join(lines)
 
@@ -565,7 +633,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DB", help="print a markdown summary of a rocprofv3 database")
-    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "mfma"])
+    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "traffic-json", "mfma"],
+                    help="summary kind; traffic modes take the FETCH_SIZE and WRITE_SIZE databases, comma-separated")
     args = ap.parse_args()
     if args.summarize_rocprof:
         print(summarize_rocprof(args.summarize_rocprof, args.mode))
