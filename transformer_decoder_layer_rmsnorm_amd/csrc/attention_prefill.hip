@@ -306,6 +306,103 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
         __syncthreads();
     };
 
+    // One step over a tile with no mask and every key block live.  Between the rescale test and the
+    // barrier it has no branch, so the scheduler can interleave, on this wave's own issue slots,
+    // the score MFMAs of tile t+1 with the exponentials of tile t (one MFMA, then six VALU
+    // instructions and one K fragment read, while the matrix core works through the MFMA), and the
+    // PV MFMAs with their V fragment reads.  The global loads and LDS stores are unconditional (a
+    // clamped tile index): past the last tile they refill a slot no later step reads.
+    auto fast_step = [&](int t, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB]) {
+        load_k(min(t + 2, nvis - 1));
+        load_v(min(t + 1, nvis - 1));
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, cur[i][r]);
+        {
+            float m0v, m1v;
+            pair_xor32(mt, m0v, m1v);
+            mt = fmaxf(m0v, m1v) * sl2;
+        }
+        if (__any(mt > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float corr = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= corr;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // scores of tile t+1
+        const bf16* sKb = sK + ((t + 1) & 1) * K_ELEMS + k_rd;
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+            const int kb = (KS == 1) ? i : ph;
+            const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP);
+            nxt[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int s = 1; s < 8; ++s) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKb + kb * 32 * KP + s * 16);
+                nxt[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], nxt[i], 0, 0, 0);
+            }
+            lnxt[i] = true;
+        }
+        // probabilities of tile t
+        bf16x8 pf[NKB][2];
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pf[i][hf][j] = (bf16)fast_exp2(fmaf(cur[i][8 * hf + j], sl2, -m_run));
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const bf16x2 pp = {pf[i][hf][j], pf[i][hf][j + 1]};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                }
+            }
+        // O^T += V^T P^T for tile t
+        const bf16* sVb = sV + (t & 1) * V_ELEMS + v_rd;
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+            const int kb = (KS == 1) ? i : ph;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const bf16* pv = sVb + (kb * 32 + hf * 16) * VP + db * 32;
+                    const bf16x4 v0 = lds_read_tr(pv);
+                    const bf16x4 v1 = lds_read_tr(pv + 8 * VP);
+                    const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[i][hf], o[db], 0, 0, 0);
+                }
+            }
+        }
+        // issue order: K reads ahead, then per score MFMA six VALU instructions of the softmax and
+        // one more K read; then the PV MFMAs, two V reads ahead of each
+        constexpr int NS = 8 * NKB;   // score MFMAs (= K fragment reads)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            if (k + 4 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (k + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        store_k(t & 1);
+        store_v((t + 1) & 1);
+        __syncthreads();
+    };
+
     load_k(0);
     load_v(0);
     store_k(0);
@@ -319,7 +416,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     f32x16 sa[NKB], sb[NKB];
     bool la[NKB], lb[NKB];
     s_tile(0, sa, la);
-    for (int t = 0; t < nvis; t += 2) {
+    int t = 0;
+    if constexpr (!MASKED) {
+        // Tiles wholly at or below the first query of the workgroup need no mask and have every key
+        // block live; all but the last (whose step would have no next tile to score) run the
+        // branch-free step, in pairs so the two score buffers alternate statically.
+        const int nfull = (pos0 + q0 + 1) / KT;
+        const int nfast = min(nfull, nvis - 1) & ~1;
+        for (; t < nfast; t += 2) {
+            fast_step(t, sa, sb, lb);
+            fast_step(t + 1, sb, sa, la);
+        }
+    }
+    for (; t < nvis; t += 2) {
         step(t, sa, la, sb, lb);
         if (t + 1 >= nvis) break;
         step(t + 1, sb, lb, sa, la);

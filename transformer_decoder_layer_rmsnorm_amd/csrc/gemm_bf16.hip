@@ -618,9 +618,12 @@ __device__ __forceinline__ void gemm_pp_body(const DevGemm& p, bf16* sA, bf16* s
 // workgroup of a round at once while the matrix cores idle.  Instead each half of the tile (128
 // rows: the waves of rows 0-1, then 2-3) goes to LDS as fp32 (row pitch BNo + 8 floats so the
 // two row groups of a store hit different banks), then every thread finishes 8 consecutive
-// output columns of a row with 16-byte loads and stores (8B-shaped o_proj 251 -> 243 us, down
-// 679 -> 671 us).  The plain and SwiGLU epilogues, which read nothing, measured slightly faster
-// storing from the accumulators and keep doing so.
+// output columns of a row with 16-byte loads and stores.  A half's residual chunks are all
+// requested before any of them is used (the first half's before the accumulators go to LDS, the
+// second half's as soon as the first half's registers are free): the compiler cannot move a
+// residual load above the output stores before it (it cannot tell that out and resid never
+// overlap), and loading chunk by chunk made every chunk a full memory round trip.  The plain and
+// SwiGLU epilogues, which read nothing, store from the accumulators.
 template <Epilogue EPI, int BN>
 struct PpEpi {
     static_assert(EPI != Epilogue::SwiGLU, "SwiGLU stores from the accumulators");
@@ -628,6 +631,18 @@ struct PpEpi {
     static constexpr int P = BNo + 8;      // LDS row pitch (floats)
     static constexpr int BYTES = 128 * P * 4;
 };
+// Residual chunk of 8 columns: bf16 x for o_proj, fp32 x1 for down (none for split-K slabs).
+template <Epilogue EPI> struct ResidChunk { f32x4 lo, hi; };
+template <> struct ResidChunk<Epilogue::ResidToF32> { bf16x8 v; };
+template <Epilogue EPI>
+__device__ __forceinline__ void load_resid_chunk(const DevGemm& p, int64_t o, ResidChunk<EPI>& r) {
+    if constexpr (EPI == Epilogue::ResidToF32) {
+        r.v = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.resid) + o);
+    } else if constexpr (EPI == Epilogue::ResidF32In) {
+        r.lo = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.resid) + o);
+        r.hi = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.resid) + o + 4);
+    }
+}
 template <Epilogue EPI, int BN>
 __device__ __forceinline__ void pp_store_tile(const DevGemm& p, const f32x16 (&acc)[kPpFM][PpTile<BN>::FN], int m0,
                                               int tn, int wm, int wn, int lane, float* tile) {
@@ -635,6 +650,28 @@ __device__ __forceinline__ void pp_store_tile(const DevGemm& p, const f32x16 (&a
     using E = PpEpi<EPI, BN>;
     constexpr int CPR = E::BNo / 8;             // 8-column chunks per row
     constexpr int PER = 128 * CPR / 512;        // chunks per thread and half
+    constexpr bool RESID = (EPI == Epilogue::ResidToF32 || EPI == Epilogue::ResidF32In);
+    // chunk k of this thread in half h: tile row 128 h + lr, columns c0 .. c0 + 7
+    auto chunk_at = [&](int h, int k, int& lr, int& c0, int& m, int64_t& o) {
+        const int c = (int)threadIdx.x + 512 * k;
+        lr = c / CPR;
+        c0 = (c % CPR) * 8;
+        m = m0 + 128 * h + lr;
+        o = (int64_t)m * p.N + tn * E::BNo + c0;
+    };
+    ResidChunk<EPI> rv[RESID ? PER : 1];
+    auto load_half = [&](int h) {
+        if constexpr (RESID) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                int lr, c0, m;
+                int64_t o;
+                chunk_at(h, k, lr, c0, m, o);
+                if (m < p.M) load_resid_chunk<EPI>(p, o, rv[k]);
+            }
+        }
+    };
+    load_half(0);
     __syncthreads();   // every wave is past its last LDS fragment read
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -651,21 +688,19 @@ __device__ __forceinline__ void pp_store_tile(const DevGemm& p, const f32x16 (&a
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int c = (int)threadIdx.x + 512 * k;
-            const int lr = c / CPR, c0 = (c % CPR) * 8;
-            const int m = m0 + 128 * h + lr;
+            int lr, c0, m;
+            int64_t o;
+            chunk_at(h, k, lr, c0, m, o);
             if (m < p.M) {
                 const f32x4 v0 = *reinterpret_cast<const f32x4*>(tile + lr * E::P + c0);
                 const f32x4 v1 = *reinterpret_cast<const f32x4*>(tile + lr * E::P + c0 + 4);
-                const int64_t o = (int64_t)m * p.N + tn * E::BNo + c0;
                 float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 if constexpr (EPI == Epilogue::ResidToF32) {
-                    const bf16x8 r8 = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.resid) + o);
                     f32x4 w0, w1;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        w0[e] = (float)r8[e] + v[e];
-                        w1[e] = (float)r8[4 + e] + v[4 + e];
+                        w0[e] = (float)rv[k].v[e] + v[e];
+                        w1[e] = (float)rv[k].v[4 + e] + v[4 + e];
                     }
                     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o) = w0;
                     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o + 4) = w1;
@@ -674,12 +709,10 @@ __device__ __forceinline__ void pp_store_tile(const DevGemm& p, const f32x16 (&a
                     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + o + 4) = v1;
                 } else {
                     if constexpr (EPI == Epilogue::ResidF32In) {
-                        const f32x4 r0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.resid) + o);
-                        const f32x4 r1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.resid) + o + 4);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            v[e] += r0[e];
-                            v[4 + e] += r1[e];
+                            v[e] += rv[k].lo[e];
+                            v[4 + e] += rv[k].hi[e];
                         }
                     }
                     bf16x8 b;
@@ -689,7 +722,10 @@ __device__ __forceinline__ void pp_store_tile(const DevGemm& p, const f32x16 (&a
                 }
             }
         }
-        if (h == 0) __syncthreads();   // the second half overwrites the LDS tile
+        if (h == 0) {
+            load_half(1);
+            __syncthreads();   // the second half overwrites the LDS tile
+        }
     }
 }
 
