@@ -10,8 +10,9 @@ import torch
 
 import oracle
 import seeded_inputs as si
-from gpu_support import (GpuLayer, assert_bf16_parity, assert_f32_parity, assert_rounded, check_decode_steps, log,
-                         oracle_qk_from_proj, small_bf16_cfg, to_dev, to_np)
+from gpu_support import (GpuLayer, assert_bf16_parity, assert_f32_parity, assert_rounded, check_decode_steps,
+                         check_prefill_stages_full, log, oracle_layer_prefill_parallel, oracle_qk_from_proj,
+                         small_bf16_cfg, to_dev, to_np)
 from transformer_decoder_layer_rmsnorm_amd import _native as nat
 
 pytestmark = pytest.mark.gpu
@@ -160,6 +161,54 @@ def test_bf16_hidden_5120_layer(t):
     yd, _ = gl.decode(to_dev(x[:, t:], cfg), [t], kc, vc)
     refd = oracle.layer_prefill_rows(x, gl.w_np, cfg, [(0, t)])
     assert_bf16_parity(to_np(yd)[0, 0], refd[0], "decode row at position T")
+
+
+@pytest.mark.parametrize("hq,hkv,b,t", [(16, 4, 8, 1000), (16, 8, 8, 1000), (8, 8, 16, 960), (32, 8, 2, 2100)])
+def test_bf16_attention_two_group_workgroups(hq, hkv, b, t):
+    """Causal prefills long enough for the attention form whose 8-wave workgroups run two groups
+    of waves in alternation (at least 512 workgroups): 4, 2 and 1 query heads per KV head,
+    lengths that end mid-tile, and (T = 960 with one head per KV head) a last query tile whose
+    final waves hold no query.  Every stage teacher-forced, then the whole layer."""
+    cfg = small_bf16_cfg(hq=hq, hkv=hkv, hidden=256, inter=256)
+    log(f"bf16 layer Hq{hq} Hkv{hkv} B{b} T{t} (two-group attention)")
+    gl = GpuLayer.seeded(cfg, seed=hq + t)
+    x = si.layer_input(cfg, b, t, seed=hq + t)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    check_prefill_stages_full(gl, x, y, kc, vc, ws, f"Hq{hq} Hkv{hkv}")
+    ref = oracle_layer_prefill_parallel(x, gl.w_np, cfg)
+    assert_bf16_parity(to_np(y), ref["y"], "y (whole oracle layer)")
+
+
+def test_bf16_attention_two_group_onto_cached_prefixes():
+    """The two-group attention with cached prefixes (random keys that no k_norm of this call
+    produced, so the running maximum is kept), ragged starts, one sequence with no prefix."""
+    cfg = small_bf16_cfg(hq=16, hkv=4, hidden=256, inter=256)
+    starts = [0, 300, 64, 511, 1, 700, 128, 33]
+    b, t = len(starts), 1000
+    cap = max(starts) + t
+    log(f"bf16 prefill_at two-group attention B{b} T{t} starts {starts}")
+    gl = GpuLayer.seeded(cfg, seed=44)
+    kc, vc = _random_cache(cfg, starts, cap, seed=44)
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    x = si.layer_input(cfg, b, t, seed=44)
+    y, kd, vd, _ = gl.prefill(to_dev(x, cfg), cap=cap, caches=(kd, vd), starts=starts)
+    ref, knew, _ = oracle.layer_prefill_cached(x, gl.w_np, cfg, kc, vc, starts)
+    assert_bf16_parity(to_np(y), ref, "prefill_at y (two-group attention)")
+
+
+def test_bf16_attention_two_group_large_gains():
+    """q_norm / k_norm gains large enough that the score bound exceeds 2^60: the two-group
+    attention keeps the running maximum on a plain prefill."""
+    cfg = small_bf16_cfg(hq=16, hkv=4, hidden=256, inter=256)
+    w = si.layer_weights(cfg, seed=45)
+    w["q_norm"] = si.round_to_bf16(w["q_norm"] * 6.0)
+    w["k_norm"] = si.round_to_bf16(w["k_norm"] * 6.0)
+    gl = GpuLayer(cfg, w)
+    b, t = 8, 1000
+    log(f"bf16 two-group attention with 6x q/k gains, B{b} T{t}")
+    x = si.layer_input(cfg, b, t, seed=45)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    check_prefill_stages_full(gl, x, y, kc, vc, ws, "6x gains")
 
 
 def test_bf16_causality_bit_exact():

@@ -478,6 +478,323 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     }
 }
 
+// ------------------------------------------------------------------ ping-pong form (long causal prefill)
+// Eight waves in two groups of four (one wave of each group per SIMD) share the K/V tiles of one
+// KV head.  Group 1's queries follow group 0's.  The groups run one phase apart and alternate,
+// with a barrier between phases: while one group's waves issue the matrix work of a tile (the PV
+// product of the previous tile, then the scores of this one) the other group's waves, on the same
+// SIMDs, run the softmax of their current tile on the vector ALU and stage the next K or V tile.
+// So one wave's exponentials overlap the other's MFMAs by construction instead of by chance.
+//   phase 2k:   group 0 matrix(k)                 group 1 softmax(k - 1), writes K(k + 1)
+//   phase 2k+1: group 0 softmax(k), writes V(k)   group 1 matrix(k)
+// K(t) is in LDS from phase 2t - 2 and last read in phase 2t + 1; V(t) from phase 2t + 1 to 2t + 3:
+// two slots of each suffice.  Group 1 stages every K tile, group 0 every V tile, each through two
+// sets of 16 registers, requested four phases before the LDS write (two phases left the vector
+// phase waiting on L2 and HBM latency); the barriers wait for LDS operations only.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int HPW>
+__global__ __launch_bounds__(512) void flash_prefill_pp_kernel(AttnArgs a, float sl2) {
+    constexpr int QW = 4 / HPW;          // 32-query blocks per group
+    constexpr int QG = 32 * QW;          // queries per group
+    constexpr int QB = 2 * QG;           // queries per workgroup
+    constexpr int NKB = 2;               // 32-key blocks per tile
+    __shared__ __attribute__((aligned(16))) bf16 sK[2 * K_ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2 * V_ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wl = wave & 3;
+    const int hi = wl % HPW, wq = wl / HPW;
+    const int g = a.Hq / a.Hkv;
+    const int subs = g / HPW;
+    const int nqt = (a.T + QB - 1) / QB;
+    int kvh, sub, b, qrank;
+    {
+        int r = blockIdx.x;
+        if ((a.Hkv & 7) == 0) {
+            // workgroup L runs on XCD L % 8: give each XCD whole KV heads so their K/V stay in its L2
+            const int xcd = r & 7;
+            r >>= 3;
+            const int hpx = a.Hkv >> 3;
+            const int m = r % hpx; r /= hpx;
+            sub = r % subs; r /= subs;
+            b = r % a.B; r /= a.B;
+            qrank = r;
+            kvh = xcd + 8 * m;
+        } else {
+            kvh = r % a.Hkv; r /= a.Hkv;
+            sub = r % subs; r /= subs;
+            b = r % a.B; r /= a.B;
+            qrank = r;
+        }
+    }
+    const int h = kvh * g + sub * HPW + hi;
+    const int q0 = (nqt - 1 - qrank) * QB;                  // heaviest query tiles first
+    const int qw = q0 + grp * QG + wq * 32;                 // this wave's first query
+    const int pos0 = __builtin_amdgcn_readfirstlane(seq_pos(a.pos, b));
+    const int kv_len = pos0 + min(q0 + QB, a.T);
+    const int n = (kv_len + KT - 1) / KT;                   // key tiles of the workgroup
+    const int my_pos = pos0 + qw + (lane & 31);
+    const int wave_first = pos0 + qw;
+    const int wave_last = pos0 + min(qw + 31, a.T - 1);
+    const bool wave_active = qw < a.T;                      // a last, partial query tile may leave waves idle
+    auto live = [&](int t) { return wave_active && t * KT <= wave_last; };
+
+    bf16x8 qf[8];
+    {
+        const bf16* qrow = static_cast<const bf16*>(a.qhat) +
+                           (((int64_t)b * a.Hq + h) * a.T + min(qw + (lane & 31), a.T - 1)) * HD;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + (2 * s + (lane >> 5)) * 8);
+    }
+    // Fixed-reference softmax.  When every key of the sequence was normalised by this call (no
+    // cached prefix), each score is bounded: q-hat and k-hat are gains times unit-RMS vectors of D
+    // features (rotation keeps norms), so |q-hat . k-hat| <= D max|g_q| max|g_k|.  If that bound,
+    // in log2 units, is at most 60, the probabilities 2^s need no running maximum: they neither
+    // overflow nor underflow in fp32 or bf16, and the softmax, being shift-invariant, is the same
+    // up to rounding.  The scale D^-1/2 log2(e) then goes into Q once, so each score costs one
+    // exp2, half a conversion and half a row-sum step: the vector phase shrinks to well under the
+    // matrix phase.  Otherwise (a cached prefix, or large gains) the running maximum is kept.
+    int fixed = 0;
+    if (pos0 == 0 && a.q_norm && a.k_norm) {
+        const bf16* gq = static_cast<const bf16*>(a.q_norm);
+        const bf16* gk = static_cast<const bf16*>(a.k_norm);
+        float mq = fmaxf(fabsf((float)gq[lane] + a.goff), fabsf((float)gq[lane + 64] + a.goff));
+        float mk = fmaxf(fabsf((float)gk[lane] + a.goff), fabsf((float)gk[lane + 64] + a.goff));
+        mq = wave_max(mq);
+        mk = wave_max(mk);
+        // 1.05: room for the bf16 rounding of q-hat, k-hat and the scaled Q
+        fixed = __builtin_amdgcn_readfirstlane((int)(mq * mk * (float)HD * sl2 * 1.05f <= 60.f));
+    }
+    if (fixed) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[s][e] = (bf16)((float)qf[s][e] * sl2);
+    }
+    const int64_t kv_base = ((int64_t)b * a.Hkv + kvh) * a.cap * HD;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.k_cache) + kv_base), (short)0, kv_len * HD * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.v_cache) + kv_base), (short)0, kv_len * HD * 2, 0x00020000);
+
+    // staging by one group (256 threads): chunk st_ch of keys st_row + 16 j, j < CH
+    const int tg = tid & 255;
+    const int st_row = tg >> 4, st_ch = tg & 15;
+    const int st_off = (st_row * HD + st_ch * 8) * 2;
+    // two register sets: a tile is requested four phases before its LDS write
+    int4v stg[2][CH];
+    auto load_tile = [&](int4v (&r)[CH], __amdgpu_buffer_rsrc_t rs, int t) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, st_off + (t * KT + 16 * j) * HD * 2, 0, 0);
+    };
+    auto store_k = [&](const int4v (&r)[CH], int slot) {
+        bf16* d = sK + slot * K_ELEMS + st_row * KP + st_ch * 8;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) *reinterpret_cast<int4v*>(d + 16 * j * KP) = r[j];
+    };
+    auto store_v = [&](const int4v (&r)[CH], int slot) {
+        bf16* d = sV + slot * V_ELEMS + st_row * VP + st_ch * 8;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) *reinterpret_cast<int4v*>(d + 16 * j * VP) = r[j];
+    };
+    const int k_rd = (lane & 31) * KP + (lane >> 5) * 8;
+    const int G = lane >> 4, ip = lane & 15;
+    const int v_rd = (4 * (G >> 1) + (ip >> 2)) * VP + 16 * (G & 1) + 4 * (ip & 3);
+
+    f32x16 o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_run = -1e30f;
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};   // row sum in four independent chains
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    f32x16 sacc[NKB];
+    bf16x8 pf[NKB][2];
+
+    auto scores = [&](int t) {
+        const bf16* sKb = sK + (t & 1) * K_ELEMS + k_rd;
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+            const bf16x8 kf0 = *reinterpret_cast<const bf16x8*>(sKb + i * 32 * KP);
+            sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int s = 1; s < 8; ++s) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKb + i * 32 * KP + s * 16);
+                sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[i], 0, 0, 0);
+            }
+        }
+    };
+    auto pv = [&](int t) {
+        const bf16* sVb = sV + (t & 1) * V_ELEMS + v_rd;
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) {
+                    const bf16* pv = sVb + (i * 32 + hf * 16) * VP + db * 32;
+                    const bf16x4 v0 = lds_read_tr(pv);
+                    const bf16x4 v1 = lds_read_tr(pv + 8 * VP);
+                    const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[i][hf], o[db], 0, 0, 0);
+                }
+    };
+    // matrix phase of tile t: PV of tile t - 1, then the scores of tile t
+    // Each half keeps its fragment reads ahead of the MFMAs that use them (eight V reads, i.e. four
+    // PV MFMAs, and four K reads), so the matrix core does not wait out an LDS round trip per MFMA.
+    auto matrix_phase = [&](int t) {
+        if (t >= 1 && live(t - 1)) {
+            pv(t - 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (k < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
+        if (t < n && live(t)) {
+            scores(t);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (k < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+    };
+    // softmax of tile t (probabilities into pf, row sum; with the running maximum, its lazy
+    // rescale of o)
+    auto softmax_phase = [&](int t) {
+        if (t < 0 || t >= n || !live(t)) return;
+        const int k0 = t * KT;
+        if (k0 + KT - 1 > wave_first) {
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    sacc[i][r] = key > my_pos ? -INFINITY : sacc[i][r];
+                }
+        }
+        if (fixed) {
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pf[i][hf][j] = (bf16)fast_exp2(sacc[i][8 * hf + j]);
+        } else {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[i][r]);
+            {
+                float m0v, m1v;
+                pair_xor32(mt, m0v, m1v);
+                mt = fmaxf(m0v, m1v) * sl2;
+            }
+            if (__any(mt > m_run + 8.f)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float corr = fast_exp2(m_run - m_new);
+                m_run = m_new;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) lsum[c] *= corr;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+            }
+#pragma unroll
+            for (int i = 0; i < NKB; ++i)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        pf[i][hf][j] = (bf16)fast_exp2(fmaf(sacc[i][8 * hf + j], sl2, -m_run));
+        }
+#pragma unroll
+        for (int i = 0; i < NKB; ++i)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const bf16x2 pp = {pf[i][hf][j], pf[i][hf][j + 1]};
+                    float& acc = lsum[(j >> 1) & 3];
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+                }
+    };
+    // vector phase of tile t (register set t & 1): this group's staging, then the softmax of tile t.
+    // Group 0 writes V(t) and requests V(t + 2); group 1 writes K(t + 2) (slot t & 1) and requests
+    // K(t + 4).
+    auto vector_phase = [&](int t, int4v (&r)[CH]) {
+        if (grp == 0) {
+            if (t >= 0 && t < n) {
+                store_v(r, t & 1);
+                if (t + 2 < n) load_tile(r, vrs, t + 2);
+            }
+        } else if (t + 2 < n) {
+            store_k(r, t & 1);
+            if (t + 4 < n) load_tile(r, krs, t + 4);
+        }
+        softmax_phase(t);
+    };
+
+    // prologue: K(0) in LDS; group 0 holds V(0), V(1), group 1 K(1), K(2) in its registers
+    if (grp == 1) {
+        load_tile(stg[0], krs, 0);
+        store_k(stg[0], 0);
+        if (n > 1) load_tile(stg[1], krs, 1);
+        if (n > 2) load_tile(stg[0], krs, 2);
+    } else {
+        load_tile(stg[0], vrs, 0);
+        if (n > 1) load_tile(stg[1], vrs, 1);
+    }
+    lds_barrier();
+    // Every wave runs matrix(k), vector(k) in turn; group 1 starts one phase later (its vector
+    // phase of tile -1 stages K(1)) and group 0 ends with one more barrier, so both pass the same
+    // barriers and phase j pairs group 0's work of step j / 2 with group 1's of step (j - 1) / 2.
+    // Unrolled by two so each step's register set is fixed.
+    if (grp == 1) {
+        vector_phase(-1, stg[1]);
+        lds_barrier();
+    }
+    for (int k = 0; k <= n; k += 2) {
+        matrix_phase(k);
+        lds_barrier();
+        vector_phase(k, stg[0]);
+        lds_barrier();
+        if (k + 1 <= n) {
+            matrix_phase(k + 1);
+            lds_barrier();
+            vector_phase(k + 1, stg[1]);
+            lds_barrier();
+        }
+    }
+    if (grp == 0) lds_barrier();
+
+    // normalise and store: lane holds d = db*32 + 8(r/4) + 4(lane/32) + r%4 of its query
+    float l0v, l1v;
+    pair_xor32((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]), l0v, l1v);
+    const float inv = 1.0f / (l0v + l1v);
+    const int q = qw + (lane & 31);
+    if (wave_active && q < a.T) {
+        bf16* orow = static_cast<bf16*>(a.out) + ((int64_t)b * a.T + q) * a.Hq * HD + (int64_t)h * HD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[db][4 * rq + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * rq + 4 * (lane >> 5)) = v4;
+            }
+    }
+}
+
 template <bool MASKED>
 hipError_t launch_hpw(const AttnArgs& a, int hpw, bool split, dim3 grid, float scale_log2, bool pair_tiles,
                       hipStream_t stream) {
@@ -514,6 +831,19 @@ hipError_t launch_attention_prefill_bf16(const AttnArgs& a, hipStream_t stream) 
     const bool pair_tiles = wgs <= 512;   // two workgroups per CU on 256 CUs
     // the masking variant only when some sequence has left padding or the layer is local
     const bool masked = a.pos.dev_pad != nullptr || a.pos.n_pad_inline > 0 || a.local.window > 0;
+    // Long causal prefill without masks: the ping-pong form, one 8-wave workgroup per CU, when it
+    // still gives at least two workgroups per CU over the grid.
+    if (!masked) {
+        const int64_t qb_pp = 64 * (4 / hpw);
+        const int64_t wgs_pp = (int64_t)((a.T + qb_pp - 1) / qb_pp) * a.Hkv * (g / hpw) * a.B;
+        if (wgs_pp >= 512 && wgs_pp <= 0x7fffffff) {
+            const dim3 gpp((unsigned)wgs_pp);
+            if (hpw == 4) flash_prefill_pp_kernel<4><<<gpp, 512, 0, stream>>>(a, scale_log2);
+            else if (hpw == 2) flash_prefill_pp_kernel<2><<<gpp, 512, 0, stream>>>(a, scale_log2);
+            else flash_prefill_pp_kernel<1><<<gpp, 512, 0, stream>>>(a, scale_log2);
+            return hipGetLastError();
+        }
+    }
     if (masked) return launch_hpw<true>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
     return launch_hpw<false>(a, hpw, split, grid, scale_log2, pair_tiles, stream);
 }

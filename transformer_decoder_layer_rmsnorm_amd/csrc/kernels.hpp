@@ -162,6 +162,12 @@ struct AttnArgs {
     LocalAttn local;        // window / sinks mask; rolling decode caches
     int B, T, Hq, Hkv, D, cap;
     float scale;            // D^-1/2
+    // q_norm / k_norm gains (and their offset) of the layer, or nullptr: every q-hat and k-hat
+    // is a gain times a unit-RMS head vector (rotated), so |q-hat . k-hat| <= D max|g_q| max|g_k|,
+    // which lets the prefill attention skip the running maximum when the bound is small
+    const void* q_norm;
+    const void* k_norm;
+    float goff;
 };
 // Causal prefill: query t of sequence b sits at position pos0(b) + t and sees keys 0 .. pos.
 hipError_t launch_attention_prefill_bf16(const AttnArgs& args, hipStream_t stream);

@@ -338,6 +338,9 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     aa.D = D;
     aa.cap = cap;
     aa.scale = (float)(1.0 / std::sqrt((double)D));
+    aa.q_norm = L->w.q_norm;
+    aa.k_norm = L->w.k_norm;
+    aa.goff = gain_off;
     if (!bf) {
         STAGE("attention", launch_attention_f32(aa, s));
     } else if (decode) {
