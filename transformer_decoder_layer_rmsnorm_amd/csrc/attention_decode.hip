@@ -3,9 +3,9 @@
 // shared by the g query heads of its KV head ("lesson 6", section 3: each new token reads its
 // own sequence's cache, which nobody shares; grouping makes each byte serve g heads).
 //
-// Split-KV: workgroup (split, kv head, sequence) takes 512 consecutive keys and produces, for
-// each of the g heads, a partial output with its running max (base 2) and sum; a second kernel
-// merges the splits.  Inside a workgroup each wave owns 128 keys.  A wave reads 4 whole key
+// Split-KV: workgroup (split, kv head, sequence) takes kDecodeSplitKeys (1024) consecutive keys
+// and produces, for each of the g heads, a partial output with its running max (base 2) and sum;
+// a second kernel merges the splits.  Inside a workgroup each wave owns a quarter of the keys.  A wave reads 4 whole key
 // rows per load instruction (lane = 16-byte chunk l%16 of key l/16), so every access is a
 // fully coalesced 1 KB; the per-key dot products are finished with a butterfly over the 16
 // lanes of a key that also splits the g heads across those lanes (log2(g) fewer exchanges).
@@ -32,6 +32,7 @@ __device__ __forceinline__ int decode_kv_len(const AttnArgs& a, int b) {
     return a.local.rolling ? min(p + 1, a.cap) : p + 1;
 }
 constexpr int KPW = SK / 4;           // keys per wave
+static_assert(KPW % 64 == 0, "the softmax pass gives each lane whole keys");
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -152,17 +153,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
         vpre[i] = *reinterpret_cast<const bf16x8*>(vg + (int64_t)min(wave * KPW + 4 * i + ks, nk - 1) * HD);
     __syncthreads();
 
-    // ---- per-wave softmax statistics over its 128 keys
+    // ---- per-wave softmax statistics over its KPW keys (lane takes keys lane + 64 i)
+    constexpr int KPL = KPW / 64;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const int k1 = wave * KPW + lane, k2 = k1 + 64;
-        const float s1 = sP[k1 * G + h], s2 = sP[k2 * G + h];
-        const float m = wave_max(fmaxf(s1, s2));
+        float sv[KPL];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            sv[i] = sP[(wave * KPW + lane + 64 * i) * G + h];
+            mx = fmaxf(mx, sv[i]);
+        }
+        const float m = wave_max(mx);
         const float mref = (m == -INFINITY) ? 0.f : m;
-        const float p1 = fast_exp2(s1 - mref), p2 = fast_exp2(s2 - mref);
-        sP[k1 * G + h] = p1;
-        sP[k2 * G + h] = p2;
-        const float l = wave_sum(p1 + p2);
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const float pr = fast_exp2(sv[i] - mref);
+            sP[(wave * KPW + lane + 64 * i) * G + h] = pr;
+            ls += pr;
+        }
+        const float l = wave_sum(ls);
         if (lane == 0) {
             sM[wave][h] = m;
             sL[wave][h] = l;

@@ -805,23 +805,28 @@ __global__ __launch_bounds__(512) void gemm_qkv_qkrope_pp_kernel(DevGemm p, QkPp
 }
 
 // ------------------------------------------------------------------ skinny (M <= 64)
-template <Epilogue EPI, int MG, int NW>
+// Weight streaming for decode-sized M: a workgroup owns 16 output columns (16 weight rows, or 16
+// gate and 16 up rows) over the whole K; its NW waves take interleaved 32-k chunks, so the
+// workgroup reads its rows as runs of NW * 64 contiguous bytes.  The loop is software-pipelined
+// D chunks deep: chunk i's loads are issued when chunk i - D is consumed, so a wave always has
+// D chunks (D KB of weights per matrix) in flight instead of emptying its queue every few chunks;
+// with one workgroup per CU that is what keeps HBM busy.
+template <Epilogue EPI, int MG, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
     constexpr int NB = DUAL ? 2 : 1;
     __shared__ float red[NB][NW][MG][256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16;
-    // the waves take interleaved 32-k chunks, so a workgroup reads its 16 weight rows as runs of
-    // NW * 64 contiguous bytes (whole cache lines) rather than NW distant 64-byte pieces
     const int k0 = wave * 32 + 8 * (lane >> 4);
+    const int niter = p.K / (32 * NW);   // the launcher checks that 32 NW divides K
 
     const bf16* brow[NB];
     if constexpr (DUAL) {
-        brow[0] = p.b[0] + (int64_t)(n0 + (lane & 15)) * p.K;
-        brow[NB - 1] = p.b[1] + (int64_t)(n0 + (lane & 15)) * p.K;
+        brow[0] = p.b[0] + (int64_t)(n0 + (lane & 15)) * p.K + k0;
+        brow[NB - 1] = p.b[1] + (int64_t)(n0 + (lane & 15)) * p.K + k0;
     } else {
-        brow[0] = seg_row(p, n0 + (lane & 15));
+        brow[0] = seg_row(p, n0 + (lane & 15)) + k0;
     }
     const bf16* arow[MG];
     bool avalid[MG];
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
     for (int mg = 0; mg < MG; ++mg) {
         const int r = mg * 16 + (lane & 15);
         avalid[mg] = r < p.M;
-        arow[mg] = p.a + (int64_t)min(r, p.M - 1) * p.K;
+        arow[mg] = p.a + (int64_t)min(r, p.M - 1) * p.K + k0;
     }
 
     f32x4 acc[NB][MG];
@@ -838,21 +843,39 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) acc[nb][mg] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const bf16x8 zero = {};
-#pragma unroll 4
-    for (int k = k0; k < p.K; k += 32 * NW) {
-        bf16x8 bv[NB];
+    bf16x8 bq[D][NB], aq[D][MG];
+    auto issue = [&](int slot, int it) {
+        const int64_t k = (int64_t)it * (32 * NW);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const bf16x8*>(brow[nb] + k);
+        for (int nb = 0; nb < NB; ++nb) bq[slot][nb] = *reinterpret_cast<const bf16x8*>(brow[nb] + k);
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) aq[slot][mg] = *reinterpret_cast<const bf16x8*>(arow[mg] + k);
+    };
+    const bf16x8 zero = {};
+    auto consume = [&](int slot) {
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg) {
-            bf16x8 av = *reinterpret_cast<const bf16x8*>(arow[mg] + k);
-            if (!avalid[mg]) av = zero;
+            const bf16x8 av = avalid[mg] ? aq[slot][mg] : zero;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                acc[nb][mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[nb], acc[nb][mg], 0, 0, 0);
+                acc[nb][mg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[slot][nb], acc[nb][mg], 0, 0, 0);
+        }
+    };
+    // niter is a multiple of D (the launcher picks D so): the steady loop has no tail tests, so
+    // the compiler's wait before each chunk counts only the loads issued after that chunk's
+    // instead of draining the queue at the loop head
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(i, i);
+    for (int base = 0; base + D < niter; base += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            consume(i);
+            issue(i, base + D + i);
+            __builtin_amdgcn_sched_barrier(0);   // keep each refill right after its chunk's product
         }
     }
+#pragma unroll
+    for (int i = 0; i < D; ++i) consume(i);
     // 16x16 accumulator layout: lane l, register i holds row 4*(l/16) + i, column l%16.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -881,6 +904,73 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
     }
 }
 
+// Split-K skinny product for M <= 16.  With 16 columns per workgroup every workgroup reads all of
+// the activations, as many bytes as its weights, and those L2-resident loads take half of the
+// vector-memory slots that should be keeping weight bytes in flight.  Here a unit is a column
+// group of 16 CG outputs (16 CG weight rows) over one k slice of 32 NW NIT: each activation
+// fragment feeds CG weight fragments, every load of the slice is issued before the first
+// product, and the units still number several per CU.  Unit (group, slice) writes its fp32
+// partial sums into slab `slice` of p.out ([kslices][M][N]); the kernel that consumes the
+// projection adds the slabs in slice order (the split-K form of the prefill GEMMs, reduced the
+// same way).
+template <int CG, int NW, int NIT>
+__global__ __launch_bounds__(NW * 64) void gemv_splitk_kernel(DevGemm p, int kslices) {
+    constexpr int NT = NW * 64;
+    constexpr int KL = 32 * NW * NIT;                // k slice
+    constexpr int OUT = (CG * 256 + NT - 1) / NT;    // tile values per thread (the last may be idle)
+    constexpr bool FULL = CG * 256 % NT == 0;
+    __shared__ float red[NW][CG][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int group = (int)blockIdx.x / kslices, ks = (int)blockIdx.x % kslices;
+    const int n0 = group * 16 * CG;
+    const int kb = ks * KL + wave * 32 + 8 * (lane >> 4);
+
+    const bf16* brow[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) brow[c] = seg_row(p, n0 + 16 * c + (lane & 15)) + kb;
+    const bool avalid = (lane & 15) < p.M;
+    const bf16* arow = p.a + (int64_t)min(lane & 15, p.M - 1) * p.K + kb;
+
+    bf16x8 aq[NIT], bq[NIT][CG];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        aq[it] = *reinterpret_cast<const bf16x8*>(arow + it * 32 * NW);
+#pragma unroll
+        for (int c = 0; c < CG; ++c) bq[it][c] = *reinterpret_cast<const bf16x8*>(brow[c] + it * 32 * NW);
+    }
+    f32x4 acc[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 zero = {};
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const bf16x8 av = avalid ? aq[it] : zero;
+#pragma unroll
+        for (int c = 0; c < CG; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[it][c], acc[c], 0, 0, 0);
+    }
+    // 16x16 accumulator layout: lane l, register i holds row 4*(l/16) + i, column l%16
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][c][(4 * (lane >> 4) + i) * 16 + (lane & 15)] = acc[c][i];
+    __syncthreads();
+    // thread t finishes values t + NT j of the tile: block (value / 256), row (value % 256) / 16,
+    // column value % 16
+    float* slab = static_cast<float*>(p.out) + (int64_t)ks * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < OUT; ++j) {
+        const int idx = threadIdx.x + NT * j;
+        if (!FULL && idx >= CG * 256) break;
+        const int c = idx >> 8, e = idx & 255;
+        const int row = e >> 4;
+        if (row >= p.M) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v += red[w][c][e];
+        slab[(int64_t)row * p.N + n0 + 16 * c + (e & 15)] = v;
+    }
+}
+
 DevGemm make_dev(const GemmArgs& g) {
     DevGemm p{};
     p.a = static_cast<const bf16*>(g.a);
@@ -900,13 +990,27 @@ DevGemm make_dev(const GemmArgs& g) {
     return p;
 }
 
+template <Epilogue EPI, int MG, int NW>
+void launch_gemv_depth(const DevGemm& p, unsigned grid, hipStream_t s) {
+    const int niter = p.K / (32 * NW);
+    if (niter % 8 == 0)
+        gemv_bf16_kernel<EPI, MG, NW, 8><<<grid, NW * 64, 0, s>>>(p);
+    else if (niter % 4 == 0)
+        gemv_bf16_kernel<EPI, MG, NW, 4><<<grid, NW * 64, 0, s>>>(p);
+    else if (niter % 2 == 0)
+        gemv_bf16_kernel<EPI, MG, NW, 2><<<grid, NW * 64, 0, s>>>(p);
+    else
+        gemv_bf16_kernel<EPI, MG, NW, 1><<<grid, NW * 64, 0, s>>>(p);
+}
+
 template <Epilogue EPI, int MG>
 hipError_t launch_gemv_mg(const DevGemm& p, hipStream_t s) {
     const unsigned grid = (unsigned)(p.N / 16);
+    if (p.K <= 0 || p.N % 16) return hipErrorInvalidValue;
     if (p.K % (32 * 8) == 0)
-        gemv_bf16_kernel<EPI, MG, 8><<<grid, 512, 0, s>>>(p);
+        launch_gemv_depth<EPI, MG, 8>(p, grid, s);
     else if (p.K % (32 * 4) == 0)
-        gemv_bf16_kernel<EPI, MG, 4><<<grid, 256, 0, s>>>(p);
+        launch_gemv_depth<EPI, MG, 4>(p, grid, s);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -1031,15 +1135,62 @@ int gemm_bf16_splits(int M, int N, int K) {
     return tiles128 < 256 ? 2 : 1;
 }
 
+// Geometry of the split-K skinny product: column groups of 64 outputs and k slices of 1024 while
+// that leaves at least kSkinnyUnits units, otherwise shorter slices, then narrower groups; no
+// split (kslices 0) when no geometry divides the shape or one slice would cover K.
+constexpr int kSkinnyUnits = 512;
+SkinnyPlan skinny_plan(int M, int N, int K) {
+    SkinnyPlan pl{};
+    if (M <= 0 || M > 16 || K <= 0 || N <= 0) return pl;
+    // candidates in order of preference: the first with kSkinnyUnits units, else the one with
+    // the most
+    int best_cg = 0, best_nit = 0;
+    long best = 0;
+    bool enough = false;
+    for (int cg = 4; cg >= 1 && !enough; cg /= 2)
+        for (int nit = 4; nit >= 1 && !enough; nit /= 2) {
+            if (N % (16 * cg) || K % (256 * nit)) continue;
+            const long units = (long)(N / (16 * cg)) * (K / (256 * nit));
+            enough = units >= kSkinnyUnits;
+            if (enough || units > best) {
+                best = units;
+                best_cg = cg;
+                best_nit = nit;
+            }
+        }
+    if (best == 0 || K / (256 * best_nit) < 2) return pl;
+    pl.cg = best_cg;
+    pl.nit = best_nit;
+    pl.kslices = K / (256 * best_nit);
+    pl.groups = N / (16 * best_cg);
+    return pl;
+}
+
+template <int CG>
+void launch_splitk_cg(const DevGemm& p, const SkinnyPlan& pl, hipStream_t s) {
+    const unsigned grid = (unsigned)(pl.groups * pl.kslices);
+    if (pl.nit == 4) gemv_splitk_kernel<CG, 8, 4><<<grid, 512, 0, s>>>(p, pl.kslices);
+    else if (pl.nit == 2) gemv_splitk_kernel<CG, 8, 2><<<grid, 512, 0, s>>>(p, pl.kslices);
+    else gemv_splitk_kernel<CG, 8, 1><<<grid, 512, 0, s>>>(p, pl.kslices);
+}
+
 hipError_t launch_gemv_bf16(const GemmArgs& g, hipStream_t s) {
     if (g.M <= 0) return hipSuccess;
     DevGemm p = make_dev(g);
+    if (g.epi == Epilogue::PartialF32) {   // split-K slabs (M <= 16, skinny_plan's geometry)
+        const SkinnyPlan pl = skinny_plan(g.M, g.N, g.K);
+        if (pl.kslices < 2 || pl.kslices != g.splits) return hipErrorInvalidValue;
+        if (pl.cg == 4) launch_splitk_cg<4>(p, pl, s);
+        else if (pl.cg == 2) launch_splitk_cg<2>(p, pl, s);
+        else launch_splitk_cg<1>(p, pl, s);
+        return hipGetLastError();
+    }
     switch (g.epi) {
         case Epilogue::Store: return launch_gemv_epi<Epilogue::Store>(p, s);
         case Epilogue::ResidToF32: return launch_gemv_epi<Epilogue::ResidToF32>(p, s);
         case Epilogue::SwiGLU: return launch_gemv_epi<Epilogue::SwiGLU>(p, s);
         case Epilogue::ResidF32In: return launch_gemv_epi<Epilogue::ResidF32In>(p, s);
-        case Epilogue::PartialF32: return hipErrorInvalidValue;
+        case Epilogue::PartialF32: break;
     }
     return hipErrorInvalidValue;
 }

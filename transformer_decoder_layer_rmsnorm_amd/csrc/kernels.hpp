@@ -116,6 +116,14 @@ struct GemmArgs {
     int splits;             // PartialF32: K is cut into `splits` equal ranges, one fp32 slab each
 };
 
+// Split-K form of a skinny (M <= 16) projection: column groups of 16 cg outputs, kslices k
+// slices of 256 nit; kslices = 0 when the shape is not split.  launch_gemv_bf16 with the
+// PartialF32 epilogue and splits = kslices writes the [kslices][M][N] fp32 slabs.
+struct SkinnyPlan {
+    int cg, nit, kslices, groups;
+};
+SkinnyPlan skinny_plan(int M, int N, int K);
+
 hipError_t launch_gemm_bf16(const GemmArgs& args, hipStream_t stream);   // MFMA, large M
 // Split count for a bf16 projection whose partial sums can be reduced by the next kernel: 2 when
 // the output has too few 128x128 tiles to fill the CUs and K splits evenly, else 1 (no split).
@@ -143,6 +151,13 @@ struct QkRopeArgs {
                             // omega_i = theta^(-2i/rotary_dim), fp64
     const float* rope_cs;   // RopeTable::cs and ::slot of these rows, or nullptr (the fused QKV
     const int32_t* rope_slot;  // epilogue needs them; launch_qknorm_rope works them out itself)
+    // qkv_splits > 0: the projections are the sum of qkv_splits fp32 slabs [splits][M][N] at
+    // qkv_part (a split-K skinny projection), rounded to bf16 as the one-kernel form stores them
+    // and stored to qkv_sum ([M, N] bf16, the workspace's projection intermediate); bf16,
+    // head_dim 128, full split-half RoPE only
+    const float* qkv_part;
+    int qkv_splits;
+    void* qkv_sum;
 };
 hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t stream);
 // QKV projection with QK-norm + RoPE + cache write fused into its epilogue (bf16, head_dim 128,
@@ -184,6 +199,6 @@ struct DecodeAttnArgs {
 };
 hipError_t launch_attention_decode_split_bf16(const DecodeAttnArgs& args, hipStream_t stream);
 hipError_t launch_attention_decode_combine_bf16(const DecodeAttnArgs& args, hipStream_t stream);
-constexpr int kDecodeSplitKeys = 512;
+constexpr int kDecodeSplitKeys = 1024;
 
 }  // namespace q3

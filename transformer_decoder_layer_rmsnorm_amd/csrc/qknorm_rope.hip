@@ -126,6 +126,9 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// PART: the projections arrive as a.qkv_splits fp32 slabs (split-K skinny QKV), summed in slab
+// order, rounded to bf16 and also stored to a.qkv_sum here.
+template <bool PART>
 __global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
     constexpr int D = 128;
     const int tok = blockIdx.x;
@@ -171,20 +174,68 @@ __global__ __launch_bounds__(256) void qknorm_rope_d128_bf16(QkRopeArgs a) {
     bf16* v_dst = static_cast<bf16*>(a.v_cache) + ((int64_t)b * a.Hkv * a.cap + cslot) * D + 4 * j;
     const int64_t q_stride = (int64_t)a.T * D, kv_stride = (int64_t)a.cap * D;
 
-    // the wave's groups are wave, wave + 4, ...; loads for GB of them are issued first
-    constexpr int GB = 4;
-    for (int g0 = wave; g0 < ngroups; g0 += 4 * GB) {
+    // Groups of four heads: workgroup y of the token takes groups 4 y + wave + gs i (gs = 4 x the
+    // workgroups per token); loads for GB of them are issued first.  The slab form runs one group
+    // per wave (gridDim.y covers them) so that all of its slab loads are in flight at once.
+    constexpr int GB = PART ? 1 : 4;
+    const int gs = 4 * (int)gridDim.y;
+    for (int g0 = 4 * (int)blockIdx.y + wave; g0 < ngroups; g0 += gs * GB) {
         bf16x4 lo[GB], hi[GB];
+        if constexpr (PART) {
+            const float* psrc = a.qkv_part + (int64_t)tok * nheads * D + 4 * j;
+            const int64_t slab = (int64_t)a.B * a.T * nheads * D;
+            f32x4 slo[GB], shi[GB];
 #pragma unroll
-        for (int i = 0; i < GB; ++i) {
-            const int h = min(4 * (g0 + 4 * i) + slot, nheads - 1);
-            lo[i] = *reinterpret_cast<const bf16x4*>(src + h * D);
-            hi[i] = *reinterpret_cast<const bf16x4*>(src + h * D + 64);
+            for (int i = 0; i < GB; ++i) slo[i] = shi[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // eight slabs' loads are issued before their sums (in slab order)
+            constexpr int SU = 8;
+            for (int sp0 = 0; sp0 < a.qkv_splits; sp0 += SU) {
+                f32x4 plo[SU][GB], phi[SU][GB];
+#pragma unroll
+                for (int u = 0; u < SU; ++u)
+#pragma unroll
+                    for (int i = 0; i < GB; ++i) {
+                        const int h = min(4 * (g0 + gs * i) + slot, nheads - 1);
+                        const int sp = min(sp0 + u, a.qkv_splits - 1);
+                        plo[u][i] = *reinterpret_cast<const f32x4*>(psrc + sp * slab + h * D);
+                        phi[u][i] = *reinterpret_cast<const f32x4*>(psrc + sp * slab + h * D + 64);
+                    }
+#pragma unroll
+                for (int u = 0; u < SU; ++u)
+                    if (sp0 + u < a.qkv_splits) {
+#pragma unroll
+                        for (int i = 0; i < GB; ++i) {
+                            slo[i] += plo[u][i];
+                            shi[i] += phi[u][i];
+                        }
+                    }
+            }
+            bf16* sum = static_cast<bf16*>(a.qkv_sum) + (int64_t)tok * nheads * D + 4 * j;
+#pragma unroll
+            for (int i = 0; i < GB; ++i) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo[i][e] = (bf16)slo[i][e];
+                    hi[i][e] = (bf16)shi[i][e];
+                }
+                if (g0 + gs * i < ngroups && 4 * (g0 + gs * i) + slot < nheads) {
+                    const int h = 4 * (g0 + gs * i) + slot;
+                    *reinterpret_cast<bf16x4*>(sum + h * D) = lo[i];
+                    *reinterpret_cast<bf16x4*>(sum + h * D + 64) = hi[i];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < GB; ++i) {
+                const int h = min(4 * (g0 + gs * i) + slot, nheads - 1);
+                lo[i] = *reinterpret_cast<const bf16x4*>(src + h * D);
+                hi[i] = *reinterpret_cast<const bf16x4*>(src + h * D + 64);
+            }
         }
 #pragma unroll
         for (int i = 0; i < GB; ++i) {
-            if (g0 + 4 * i >= ngroups) break;     // uniform across the wave
-            const int h = 4 * (g0 + 4 * i) + slot;
+            if (g0 + gs * i >= ngroups) break;    // uniform across the wave
+            const int h = 4 * (g0 + gs * i) + slot;
             float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { x[e] = (float)lo[i][e]; x[4 + e] = (float)hi[i][e]; }
@@ -222,8 +273,13 @@ hipError_t launch_qknorm_rope(const QkRopeArgs& args, DType t, hipStream_t strea
     if (args.D > 128 || (args.D & 1)) return hipErrorInvalidValue;
     if (args.rotary_dim > args.D || (args.rotary_dim & 1) || args.rotary_dim < 0) return hipErrorInvalidValue;
     // the vectorised kernel covers the Qwen3 layout (all 128 features rotated, split-half pairs)
-    if (t == DType::BF16 && args.D == 128 && args.rotary_dim == 128 && !args.adjacent)
-        qknorm_rope_d128_bf16<<<(unsigned)tokens, 256, 0, stream>>>(args);
+    const bool d128 = t == DType::BF16 && args.D == 128 && args.rotary_dim == 128 && !args.adjacent;
+    if (args.qkv_splits > 0) {
+        if (!d128 || !args.qkv_part || !args.qkv_sum) return hipErrorInvalidValue;
+        const int ngroups = (args.Hq + 2 * args.Hkv + 3) / 4;
+        qknorm_rope_d128_bf16<true><<<dim3((unsigned)tokens, (unsigned)((ngroups + 3) / 4)), 256, 0, stream>>>(args);
+    } else if (d128)
+        qknorm_rope_d128_bf16<false><<<(unsigned)tokens, 256, 0, stream>>>(args);
     else if (t == DType::BF16)
         qknorm_rope_kernel<bf16><<<(unsigned)tokens, 256, 0, stream>>>(args);
     else

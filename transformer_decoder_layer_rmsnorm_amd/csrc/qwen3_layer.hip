@@ -118,6 +118,15 @@ struct Layout {
     int splits;
 };
 
+// Split-K geometry of the skinny (M <= 16, bf16) QKV projection, whose fp32 slabs the QK-norm +
+// RoPE kernel adds (head_dim 128 split-half RoPE only); kslices = 0: not split.  o_proj and
+// down keep the one-kernel form: their slabs would need another pass over the residual.
+SkinnyPlan skinny_qkv_split(const qwen3_config& c, int64_t M) {
+    if (c.dtype != QWEN3_BF16 || M > 16 || c.head_dim != 128 || c.rotary_dim != 128 || c.rope_adjacent_pairs)
+        return SkinnyPlan{};
+    return skinny_plan((int)M, (c.num_attention_heads + 2 * c.num_key_value_heads) * c.head_dim, c.hidden_size);
+}
+
 Layout make_layout(const qwen3_config& c, int64_t B, int64_t T, int64_t cap) {
     const int64_t M = B * T;
     const int64_t es = c.dtype == QWEN3_BF16 ? 2 : 4;
@@ -140,7 +149,9 @@ Layout make_layout(const qwen3_config& c, int64_t B, int64_t T, int64_t cap) {
                                 gemm_bf16_splits((int)M, (int)H, (int)I));
         splits = so > 1 ? so : 0;
     }
-    L.part_gemm = take(splits * M * H * 4);
+    // or the slabs of a split skinny QKV projection
+    const int64_t skinny_bytes = (int64_t)skinny_qkv_split(c, M).kslices * M * (Hq + 2 * Hkv) * D * 4;
+    L.part_gemm = take(std::max<int64_t>(splits * M * H * 4, skinny_bytes));
     L.prefill_end = off;
     L.splits = cap > 0 ? (int)((cap + kDecodeSplitKeys - 1) / kDecodeSplitKeys) : 0;
     L.lens = take(B * 4 * 3);   // first slots, padding starts, padding lengths
@@ -271,6 +282,7 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
         if (!bf) return launch_gemm_f32(g, s);
         return g.M <= 64 ? launch_gemv_bf16(g, s) : launch_gemm_bf16(g, s);
     };
+    float* part = reinterpret_cast<float*>(ws + lay.part_gemm);   // split-K fp32 slabs
     qwen3_status st;
     const bool prof = allow_profiling && L->profiling;
 #define STAGE(name, expr)                                    \
@@ -320,6 +332,16 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     }
     if (fused_qkv) {
         STAGE("gemm_qkv_qknorm_rope", launch_gemm_qkv_qkrope(gq, qa, s));
+    } else if (const SkinnyPlan sq = skinny_qkv_split(c, M); sq.kslices > 1) {
+        GemmArgs gs = gq;
+        gs.out = part;
+        gs.epi = Epilogue::PartialF32;
+        gs.splits = sq.kslices;
+        qa.qkv_part = part;
+        qa.qkv_splits = sq.kslices;
+        qa.qkv_sum = qkv;
+        STAGE("gemm_qkv", launch_gemv_bf16(gs, s));
+        STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
     } else {
         STAGE("gemm_qkv", proj(gq));
         STAGE("qknorm_rope", launch_qknorm_rope(qa, t, s));
@@ -357,7 +379,6 @@ qwen3_status run_layer(qwen3_layer* L, const void* x, void* y, int B, int T, voi
     }
     // o_proj + residual.  With few output tiles the K range is split and the fp32 partial sums are
     // added to the residual inside the post-attention RMSNorm (which reads x1 anyway).
-    float* part = reinterpret_cast<float*>(ws + lay.part_gemm);
     const int so = bf ? gemm_bf16_splits(M, H, Hq * D) : 1;
     if (so > 1) {
         GemmArgs go = gemm(attn, {L->w.o_proj}, {H}, part, nullptr, M, H, Hq * D, Epilogue::PartialF32);
