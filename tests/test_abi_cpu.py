@@ -289,7 +289,8 @@ def test_decode_noalloc_rejects_before_any_device_call(layer):
     up on a device (there is none here)."""
     L = nat.lib()
     lens = (ctypes.c_int32 * 64)(*([32768] * 64))
-    st = L.qwen3_layer_decode_noalloc(layer, FAKE, FAKE, 64, lens, FAKE, FAKE, 32769, None)
+    # 64 sequences over 65537 cache slots: 65 key splits of 1024, about 34 MB of partials
+    st = L.qwen3_layer_decode_noalloc(layer, FAKE, FAKE, 64, lens, FAKE, FAKE, 65537, None)
     assert st == nat.QWEN3_ERR_WORKSPACE_TOO_SMALL, err()
     assert "32 MiB" in err() or "bytes of scratch" in err()
     one = (ctypes.c_int32 * 1)(5)
