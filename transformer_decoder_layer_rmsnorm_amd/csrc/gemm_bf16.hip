@@ -904,6 +904,112 @@ __global__ __launch_bounds__(NW * 64) void gemv_bf16_kernel(DevGemm p) {
     }
 }
 
+// Skinny product for M <= 16 with whole-line weight loads.  In the MFMA operand layout a
+// 16-column fragment is 16 rows x 64 bytes, so a load instruction that feeds the matrix core
+// directly reads half of each of 16 cache lines, and the other halves come with another wave's
+// instruction: every weight line crosses from L2 twice.  Here a wave reads its 16 (SwiGLU: 16
+// gate and 16 up) weight rows over a 256-k stage as instructions of two rows x 512 contiguous
+// bytes, puts them in its own LDS buffer (row pitch 528 bytes: the 16 rows of a fragment read
+// fall on distinct banks) and reads the fragments back from there; no barrier is needed since
+// a wave's LDS operations complete in order.  Waves take interleaved stages, D of them in
+// flight per wave; the activations (16 rows) are read in the operand layout as before.
+template <Epilogue EPI, int D>
+__global__ __launch_bounds__(512) void gemv_lds_kernel(DevGemm p) {
+    constexpr int NW = 8;
+    constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
+    constexpr int NB = DUAL ? 2 : 1;
+    constexpr int R = 16 * NB;            // weight rows of the workgroup
+    constexpr int NI = R / 2;             // weight loads per stage
+    constexpr int KS = 256;               // k per stage
+    constexpr int PITCH = KS * 2 + 16;    // LDS row pitch, bytes
+    __shared__ __attribute__((aligned(16))) char rows[NW][R * PITCH];
+    __shared__ float red[NB][NW][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int niter = p.K / (KS * NW);   // a multiple of D (the launcher checks)
+
+    // weight load i of a stage: tile rows 2i (lanes 0-31) and 2i+1 (lanes 32-63), 16 bytes a lane
+    const bf16* wsrc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        const int n = n0 + (r & 15);
+        const bf16* base;
+        if constexpr (DUAL) base = p.b[r >> 4] + (int64_t)n * p.K;
+        else base = seg_row(p, n);
+        wsrc[i] = base + wave * KS + (lane & 31) * 8;
+    }
+    const bool avalid = (lane & 15) < p.M;
+    const bf16* asrc = p.a + (int64_t)min(lane & 15, p.M - 1) * p.K + wave * KS + 8 * (lane >> 4);
+    char* my = rows[wave];
+
+    int4v wq[D][NI];
+    bf16x8 aq[D][KS / 32];
+    auto issue = [&](int slot, int it) {
+        const int64_t k = (int64_t)it * (KS * NW);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) wq[slot][i] = *reinterpret_cast<const int4v*>(wsrc[i] + k);
+#pragma unroll
+        for (int q = 0; q < KS / 32; ++q) aq[slot][q] = *reinterpret_cast<const bf16x8*>(asrc + k + 32 * q);
+    };
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 zero = {};
+    auto consume = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            *reinterpret_cast<int4v*>(my + (2 * i + (lane >> 5)) * PITCH + (lane & 31) * 16) = wq[slot][i];
+#pragma unroll
+        for (int q = 0; q < KS / 32; ++q) {
+            const bf16x8 av = avalid ? aq[slot][q] : zero;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const bf16x8 bv =
+                    *reinterpret_cast<const bf16x8*>(my + ((lane & 15) + 16 * nb) * PITCH + 64 * q + 16 * (lane >> 4));
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(i, i);
+    for (int base = 0; base + D < niter; base += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            consume(i);
+            issue(i, base + D + i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) consume(i);
+
+    // 16x16 accumulator layout: lane l, register i holds row 4*(l/16) + i, column l%16
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[nb][wave][(4 * (lane >> 4) + i) * 16 + (lane & 15)] = acc[nb][i];
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int e = threadIdx.x;
+        const int row = e >> 4, col = n0 + (e & 15);
+        if (row < p.M) {
+            float sum[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                sum[nb] = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sum[nb] += red[nb][w][e];
+            }
+            if constexpr (DUAL) {
+                static_cast<bf16*>(p.out)[(int64_t)row * p.N + col] = (bf16)silu_mul(sum[0], sum[NB - 1]);
+            } else {
+                epilogue_store<EPI>(p, row, col, sum[0]);
+            }
+        }
+    }
+}
+
 // Split-K skinny product for M <= 16.  With 16 columns per workgroup every workgroup reads all of
 // the activations, as many bytes as its weights, and those L2-resident loads take half of the
 // vector-memory slots that should be keeping weight bytes in flight.  Here a unit is a column
@@ -1018,6 +1124,13 @@ hipError_t launch_gemv_mg(const DevGemm& p, hipStream_t s) {
 
 template <Epilogue EPI>
 hipError_t launch_gemv_epi(const DevGemm& p, hipStream_t s) {
+    if (p.M <= 16 && p.K > 0 && p.K % 2048 == 0 && p.N % 16 == 0) {   // whole-line weight loads
+        const unsigned grid = (unsigned)(p.N / 16);
+        // two stages in flight per wave; SwiGLU's 32 rows a stage leave registers for one
+        if (EPI != Epilogue::SwiGLU && (p.K / 2048) % 2 == 0) gemv_lds_kernel<EPI, 2><<<grid, 512, 0, s>>>(p);
+        else gemv_lds_kernel<EPI, 1><<<grid, 512, 0, s>>>(p);
+        return hipGetLastError();
+    }
     if (p.M <= 16) return launch_gemv_mg<EPI, 1>(p, s);
     if (p.M <= 32) return launch_gemv_mg<EPI, 2>(p, s);
     if (p.M <= 64) return launch_gemv_mg<EPI, 4>(p, s);
