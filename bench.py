@@ -510,12 +510,12 @@ ROOFLINE_KERNELS = {
                                                             "transformer_decoder_layer_rmsnorm_amd/csrc/gemm_bf16.hip"),
     ("flash_prefill_kernel<2, 2, false>", (512, 1, 1)): ("attention", "qwen3-0.6b-layer-prefill",
                                                         "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
-    ("flash_prefill_kernel<2, 1, false>", (2048, 1, 1)): ("attention", "qwen3-0.6b-stack28-prefill",
-                                                         "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
-    ("flash_prefill_kernel<4, 1, false>", (2048, 1, 1)): ("attention", "qwen3-8b-layer-prefill",
-                                                         "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
+    ("flash_prefill_pp_kernel<2>", (1024, 1, 1)): ("attention", "qwen3-0.6b-stack28-prefill",
+                                                  "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
+    ("flash_prefill_pp_kernel<4>", (1024, 1, 1)): ("attention", "qwen3-8b-layer-prefill",
+                                                  "transformer_decoder_layer_rmsnorm_amd/csrc/attention_prefill.hip"),
 }
-DECODE_KERNELS = (("decode_split_kernel<4>", (65, 8, 16)), ("decode_combine_kernel", (32, 16, 1)))
+DECODE_KERNELS = (("decode_split_kernel<4>", (33, 8, 16)), ("decode_combine_kernel", (32, 16, 1)))
 
 
 def _traffic(dbs, mode):
