@@ -562,7 +562,8 @@ def _traffic(dbs, mode):
 
 def summarize_rocprof(db, mode):
     """Markdown table from a rocprofv3 database of this benchmark: 'trace' (durations per
-    kernel and grid), 'traffic' (FETCH_SIZE / WRITE_SIZE per dispatch), or 'mfma' (MFMA
+    kernel and grid), 'traffic' (FETCH_SIZE / WRITE_SIZE per dispatch), 'issue' (instruction mix
+    and co-issue of the MFMA kernels), or 'mfma' (MFMA
     utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs * 256 CUs * one XCD's GRBM_GUI_ACTIVE), the
     share of SIMD cycles whose matrix pipe was busy, and the clock = one XCD's GRBM_GUI_ACTIVE /
     the dispatch's duration, meaningful for dispatches far longer than the counter overhead)."""
@@ -605,6 +606,26 @@ def summarize_rocprof(db, mode):
                 # kernel's busy cycles (rocprofv3's derived metrics take the max over XCDs)
                 agg[key[di]]["_mhz"].append(cs["GRBM_GUI_ACTIVE"] / XCD_COUNT / dur[di] * 1e3)
     avg = lambda v: sum(v) / len(v) if v else float("nan")
+    if mode == "issue":
+        # instruction mix of the kernels that use the matrix cores: VALU, transcendental and LDS
+        # instructions per MFMA instruction, MFMA busy share (as in 'mfma') and the share of
+        # MFMA-busy cycles in which the VALU also issued (SQ_VALU_MFMA_COEXEC_CYCLES)
+        lines.append("| kernel | grid (workgroups) | dispatches | avg us | VALU / MFMA | TRANS / MFMA | "
+                     "LDS / MFMA | MFMA busy % | VALU co-issue % of MFMA busy |")
+        lines.append("|---|---|---|---|---|---|---|---|---|")
+        for k in sorted(agg, key=lambda k: -avg(agg[k].get("_us", [0])) * len(agg[k].get("_us", [0]))):
+            a = agg[k]
+            mf = avg(a.get("SQ_INSTS_MFMA", []))
+            if not mf or mf != mf:
+                continue
+            gui = avg(a.get("GRBM_GUI_ACTIVE", [])) / XCD_COUNT
+            busy = avg(a.get("SQ_VALU_MFMA_BUSY_CYCLES", []))
+            util = 100.0 * busy / (4 * CU_COUNT * gui) if gui else float("nan")
+            co = 100.0 * avg(a.get("SQ_VALU_MFMA_COEXEC_CYCLES", [])) / busy if busy else float("nan")
+            lines.append(f"| `{k[0]}` | {k[1:]} | {len(a.get('GRBM_GUI_ACTIVE', []))} | {avg(a.get('_us', [])):.2f} | "
+                         f"{avg(a.get('SQ_INSTS_VALU', [])) / mf:.2f} | {avg(a.get('SQ_INSTS_VALU_TRANS_F32', [])) / mf:.2f} | "
+                         f"{avg(a.get('SQ_INSTS_LDS', [])) / mf:.2f} | {util:.1f} | {co:.1f} |")
+        return "\n".join(lines)
     lines.append("| kernel | grid (workgroups) | dispatches | avg us | MFMA busy % | clock MHz | bf16 MFMA MOPS |")
     lines.append("|---|---|---|---|---|---|---|")
     for k in sorted(agg, key=lambda k: -avg(agg[k].get("_us", [0])) * len(agg[k].get("_us", [0]))):
@@ -633,7 +654,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DB", help="print a markdown summary of a rocprofv3 database")
-    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "traffic-json", "mfma"],
+    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "traffic-json", "mfma", "issue"],
                     help="summary kind; traffic modes take the FETCH_SIZE and WRITE_SIZE databases, comma-separated")
     args = ap.parse_args()
     if args.summarize_rocprof:
