@@ -260,6 +260,33 @@ def test_bf16_decode_matches_oracle_ragged(hq, hkv):
     check_decode_steps(gl, ws, lens, kd, vd)
 
 
+@pytest.mark.parametrize("b", [1, 5, 16])
+def test_bf16_decode_skinny_kernels(b):
+    """Decode at widths where the skinny projections take their whole-line LDS-staged form (o and
+    gate/up with K = 2048: one stage in flight per wave; down with K = 4096: two) and the QKV
+    projection its split-K form whose slabs the QK-norm kernel adds (8 slices of 256): hidden 2048,
+    intermediate 4096, 16 / 8 heads, with 1, 5 and 16 sequences (token rows past the batch in the
+    16-row MFMA tiles read as zeros)."""
+    cfg = small_bf16_cfg(hq=16, hkv=8, hidden=2048, inter=4096)
+    gl = GpuLayer.seeded(cfg, seed=29)
+    rng = np.random.default_rng(29 + b)
+    lens = [int(v) for v in rng.integers(0, 700, size=b)]
+    cap = 720
+    log(f"bf16 decode hidden 2048, B{b}, lens {lens}")
+    kc = np.zeros((b, 8, cap, 128), np.float32)
+    vc = np.zeros((b, 8, cap, 128), np.float32)
+    for i, n in enumerate(lens):
+        for h in range(8):
+            kc[i, h, :n] = si.cache_block(cfg, "k", i, h, n, seed=29)
+            vc[i, h, :n] = si.cache_block(cfg, "v", i, h, n, seed=29)
+    kd, vd = to_dev(kc, cfg), to_dev(vc, cfg)
+    x = si.layer_input(cfg, b, 1, seed=29)
+    y, ws = gl.decode(to_dev(x, cfg), lens, kd, vd)
+    ref, _, _ = oracle.layer_decode(x, gl.w_np, cfg, kc, vc, lens)
+    assert_bf16_parity(to_np(y), ref, "decode y")
+    check_decode_steps(gl, ws, lens, kd, vd)
+
+
 def test_bf16_decode_continues_prefill():
     cfg = small_bf16_cfg()
     gl = GpuLayer.seeded(cfg, seed=17)
