@@ -347,6 +347,31 @@ def bench_decode(torch, si, nat, wl, steps, warmup, w_np=None):
             "kernels": kernel_table(avg, byts=decode_skinny_bytes(cfg))}
 
 
+def library_gemm(torch, cfg, m, steps, warmup, ours):
+    """Context for the projections (--library-gemm): torch.matmul, which is hipBLASLt on this
+    image, on the same M x N x K shapes in bf16 - plain products with a bf16 output, none of the
+    fused epilogues (residual in fp32, SwiGLU, QK-norm + RoPE + cache write) - beside this
+    library's stage time."""
+    h, d, i = cfg.hidden_size, cfg.head_dim, cfg.intermediate_size
+    hq, hkv = cfg.num_attention_heads, cfg.num_key_value_heads
+    shapes = {"gemm_qkv_qknorm_rope": ((hq + 2 * hkv) * d, h), "gemm_o_residual": (h, hq * d),
+              "gemm_gate_up_swiglu": (2 * i, h), "gemm_down_residual": (h, i)}
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    out = {}
+    for stage, (n, k) in shapes.items():
+        a = torch.randn((m, k), generator=gen, device="cuda").to(torch.bfloat16)
+        w = (0.02 * torch.randn((n, k), generator=gen, device="cuda")).to(torch.bfloat16)
+        ms, _ = time_steps(torch, lambda: torch.matmul(a, w.t()), steps, warmup)
+        rec = {"M": m, "N": n, "K": k, "avg_ms": round(ms, 5), "tflops": round(2 * m * n * k / (ms * 1e-3) / 1e12, 1)}
+        if stage in ours:
+            rec["this_library_ms"] = ours[stage]["avg_ms"]
+        out[stage] = rec
+        del a, w
+    torch.cuda.empty_cache()
+    return {"kind": "torch.matmul (hipBLASLt), plain bf16 products without the fused epilogues",
+            "stages": out}
+
+
 # ------------------------------------------------------------------------------ CPU baseline
 
 def cpu_info():
@@ -653,6 +678,8 @@ def main():
                     help="seconds of untimed steps before each workload's warmup steps (clock settling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy 5 times (scale for HBM byte counters)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the headline workload's projection shapes")
     ap.add_argument("--summarize-rocprof", metavar="DB", help="print a markdown summary of a rocprofv3 database")
     ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "traffic-json", "mfma", "issue"],
                     help="summary kind; traffic modes take the FETCH_SIZE and WRITE_SIZE databases, comma-separated")
@@ -749,6 +776,8 @@ def main():
     }
     if calib:
         line["copy_calibration"] = calib
+    if args.library_gemm:
+        line["library_gemm"] = library_gemm(torch, wl4.cfg, wl4.batch * wl4.seq_len, 10, 3, head["kernels"])
     if cpu:
         base = run_cpu_baselines(torch, si, nat, wls, gpu_y, inputs)
         info = cpu_info()
