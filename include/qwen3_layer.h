@@ -98,8 +98,9 @@ typedef struct qwen3_layer qwen3_layer;
  *   x1    [M, H]            residual after attention (always fp32)
  *   h2    [M, H]            post-attention RMSNorm output (dtype)
  *   act   [M, I]            silu(gate) * up (dtype)
- *   part_gemm [P, M, H]     fp32 split-K partial sums of o_proj (bf16 prefill when too
- *                           few output tiles fill the GPU; P = 0 otherwise); for bf16
+ *   part_gemm [P, M, H]     fp32 split-K partial sums of o_proj and down (bf16 prefill
+ *                           when even 64 x 128 output tiles are too few to fill the GPU;
+ *                           P = 0 otherwise); for bf16
  *                           with M <= 16 and head_dim 128, the QKV projection's split-K
  *                           slabs [P, M, (Hq+2Hkv)*D] (their bf16 sum is stored to qkv)
  *   lens  [3, B]            int32 copies of the first slots (decode cache lengths / prefill

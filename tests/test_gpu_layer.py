@@ -133,14 +133,16 @@ def test_bf16_layer_matches_oracle(hq, hkv, b, t):
     assert_bf16_parity(to_np(y), oracle.layer_prefill(x, gl.w_np, cfg)["y"], "y")
 
 
-@pytest.mark.parametrize("t", [1100, 700])
+@pytest.mark.parametrize("t", [1100, 700, 90])
 def test_bf16_hidden_5120_layer(t):
     """hidden 5120, a width of the family above 4096 (16 / 8 heads, intermediate 1024).
     T = 1100: the fused QKV epilogue on 128 x 128 tiles, fed by the input RMSNorm that also
-    writes the RoPE table, in its form for rows over 4096 wide.  T = 700: too few output tiles
-    for o_proj, whose K range is split and whose slabs the post-attention RMSNorm sums, in its
-    form for rows over 4096 wide; down split-K with the residual-sum pass.  Then one decode
-    step on the prefilled cache (skinny GEMMs with K = 5120)."""
+    writes the RoPE table, in its form for rows over 4096 wide.  T = 700: o_proj and down on the
+    deep-ring 64 x 128 tiles with the residual added in their epilogues, the last row tile
+    ragged.  T = 90: too few output tiles even for those: o_proj's K range is split and the
+    post-attention RMSNorm sums its slabs, in its form for rows over 4096 wide; down split-K with
+    the residual-sum pass.  Then one decode step on the prefilled cache (skinny GEMMs with
+    K = 5120)."""
     cfg = small_bf16_cfg(hq=16, hkv=8, hidden=5120, inter=1024)
     log(f"bf16 layer hidden 5120, B1 T{t}")
     gl = GpuLayer.seeded(cfg, seed=t)
@@ -161,6 +163,27 @@ def test_bf16_hidden_5120_layer(t):
     yd, _ = gl.decode(to_dev(x[:, t:], cfg), [t], kc, vc)
     refd = oracle.layer_prefill_rows(x, gl.w_np, cfg, [(0, t)])
     assert_bf16_parity(to_np(yd)[0, 0], refd[0], "decode row at position T")
+
+
+@pytest.mark.parametrize("b,t", [(1, 1000), (2, 750), (1, 2048)])
+def test_bf16_thin_projections_deep_ring(b, t):
+    """o_proj and down with too few 128 x 128 output tiles to fill the CUs but at least 128 tiles
+    of 64 x 128 (hidden 1024 at 1000 to 2048 tokens): the deep-ring kernel, K not split, with the
+    residual added in its epilogue (x1 = x + attn Wo^T in fp32, y = x1 + act Wd^T rounded once).
+    The last row tile is ragged at 1000 and 1500 rows; every element is checked teacher-forced."""
+    cfg = small_bf16_cfg(hq=8, hkv=4, hidden=1024, inter=3072)
+    log(f"bf16 thin projections B{b} T{t}")
+    gl = GpuLayer.seeded(cfg, seed=t + b)
+    w = gl.w_np
+    x = si.layer_input(cfg, b, t, seed=t + 2 * b)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    it = gl.intermediates(ws, b, t)
+    yn = to_np(y)
+    for s in range(b):
+        x1 = x[s] + it["attn"][s] @ w["o_proj"].T.astype(np.float64)
+        np.testing.assert_allclose(it["x1"][s], x1, rtol=1e-5, atol=2e-5)
+        yref = it["x1"][s] + it["act"][s] @ w["down_proj"].T.astype(np.float64)
+        assert_rounded(yn[s], yref, "gemm_down_residual (deep ring)")
 
 
 @pytest.mark.parametrize("hq,hkv,b,t", [(16, 4, 8, 1000), (16, 8, 8, 1000), (8, 8, 16, 960), (32, 8, 2, 2100)])

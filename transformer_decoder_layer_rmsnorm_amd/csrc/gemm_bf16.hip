@@ -804,6 +804,186 @@ __global__ __launch_bounds__(512) void gemm_qkv_qkrope_pp_kernel(DevGemm p, QkPp
     });
 }
 
+// ------------------------------------------------------------------ thin products: deep ring
+// Products with few output tiles (M x N of one to four million: the 0.6B-shaped o_proj and down at
+// 2048 tokens) give each tile little matrix work per k stage.  Here 64 x 128 tiles (four waves of
+// 32 x 64, one per SIMD) stream K through a ring of three 128-k stages loaded straight into LDS
+// two stages ahead (96 KB in flight per CU), and the residual is added from the accumulators: K
+// is not split, so there are no partial sums and no extra pass over them.  A stage is two 64-k
+// halves of 128-byte rows, XOR-swizzled by (row >> 1) & 7 as in the ping-pong kernel; A rows past
+// M read as zeros (one descriptor per 8-row group, covering its valid rows).  The first touch of
+// each operand line on an XCD misses L2, so a stage still waits on memory: a deeper ring of
+// 64-k stages (five in flight) was no faster, its extra barriers costing what the depth gained.
+constexpr int kRgBM = 64, kRgBN = 128;
+constexpr int kRgS = 3, kRgH = 2;                // ring slots; 64-k halves per stage
+constexpr int kRgHalf = (kRgBM + kRgBN) * 64;   // elements of one 64-k half
+constexpr int kRgSlot = kRgH * kRgHalf;          // elements of one stage
+
+static bool ring_fits(int M, int N, int K) {
+    if (M <= 64 || N % kRgBN || K % (64 * kRgH) || (int64_t)K * 2 * 8 >= ((int64_t)1 << 31)) return false;
+    const long tiles = (long)((M + kRgBM - 1) / kRgBM) * (N / kRgBN);
+    const long tiles128 = (long)((M + 127) / 128) * (N / 128);
+    return tiles >= 128 && tiles128 < 256;
+}
+
+template <Epilogue EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_ring_kernel(DevGemm p) {
+    static_assert(EPI == Epilogue::Store || EPI == Epilogue::ResidToF32 || EPI == Epilogue::ResidF32In,
+                  "plain and residual epilogues");
+    __shared__ __attribute__((aligned(1024))) bf16 smem[kRgS * kRgSlot];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    tile_of(p, blockIdx.x, tm, tn);
+    const int m0 = tm * kRgBM;
+    const int rowbytes = p.K * 2;
+
+    // this wave's loads of each 64-k half: A groups 2w, 2w + 1 and B groups 4w .. 4w + 3 (8 rows each)
+    int4v da[2], db[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r0 = m0 + 8 * (2 * wave + i);
+        da[i] = sgpr_desc(p.a + (int64_t)min(r0, p.M - 1) * p.K, max(0, min(8, p.M - r0)) * rowbytes);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) db[j] = sgpr_desc(seg_row(p, tn * kRgBN + 8 * (4 * wave + j)), 8 * rowbytes);
+    // lane l moves row l / 8 of its group into physical chunk l % 8 (logical chunk (l % 8) ^
+    // swz8(row)); the swizzle depends on the parity of the group
+    const int r8 = lane >> 3;
+    const int voff_even = r8 * rowbytes + (((lane & 7) ^ swz8(r8)) << 4);
+    const int voff_odd = r8 * rowbytes + (((lane & 7) ^ swz8(8 + r8)) << 4);
+    const unsigned s_lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) bf16*)smem;
+    // the 12 loads of stage st into ring slot `slot`; with live false the descriptors hold no
+    // records (zeros, nothing fetched), so every stage issues the same count
+    auto issue = [&](int st, int slot, bool live) {
+#pragma unroll
+        for (int hf = 0; hf < kRgH; ++hf) {
+            const int soff = st * (128 * kRgH) + hf * 128;
+            const unsigned base = s_lds + (unsigned)(slot * kRgSlot + hf * kRgHalf) * 2;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                int4v d = da[i];
+                d[2] = live ? d[2] : 0;
+                dma16(d, (i & 1) ? voff_odd : voff_even, soff,
+                      __builtin_amdgcn_readfirstlane(base + (unsigned)(8 * (2 * wave + i) * 64) * 2));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int4v d = db[j];
+                d[2] = live ? d[2] : 0;
+                dma16(d, (j & 1) ? voff_odd : voff_even, soff,
+                      __builtin_amdgcn_readfirstlane(base + (unsigned)((kRgBM + 8 * (4 * wave + j)) * 64) * 2));
+            }
+        }
+    };
+
+    // fragment of a 32-row block for 16-k step q of a half: row lane % 32, logical chunk
+    // 2 q + lane / 32 (the block's base row is a multiple of 32, so the swizzle is swz8(lane % 32))
+    const int fr = lane & 31;
+    int rd[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rd[q] = fr * 64 + (((2 * q + (lane >> 5)) ^ swz8(fr)) << 3);
+    const int a_off = wm * 32 * 64, b_off = (kRgBM + wn * 64) * 64;
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+    const int nst = p.K / (64 * kRgH);
+#pragma unroll
+    for (int i = 0; i < kRgS - 1; ++i) issue(i, i, i < nst);
+    int slot = 0, slot_next = kRgS - 1;
+    for (int t = 0; t < nst; ++t) {
+        vm_wait<6 * kRgH * (kRgS - 2)>();   // this wave's loads of stage t have landed
+        barrier_only();   // ... every wave's; and every wave is past its reads of stage t - 1
+        const bf16* st = smem + slot * kRgSlot;
+        // a half's 12 fragments are read together, the next half's over this half's MFMAs, so a
+        // stage waits out one LDS round trip rather than one per 16-k step
+        bf16x8 fa[kRgH][4], fb[kRgH][4][2];
+        auto read_half = [&](int hf) {
+            const bf16* h = st + hf * kRgHalf;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                fa[hf][q] = *reinterpret_cast<const bf16x8*>(h + a_off + rd[q]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) fb[hf][q][j] = *reinterpret_cast<const bf16x8*>(h + b_off + j * 32 * 64 + rd[q]);
+            }
+        };
+        read_half(0);
+        issue(t + kRgS - 1, slot_next, t + kRgS - 1 < nst);   // into the slot stage t - 1 used
+#pragma unroll
+        for (int hf = 0; hf < kRgH; ++hf) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (hf + 1 < kRgH) read_half(hf + 1);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[hf][q], fb[hf][q][j], acc[j], 0, 0, 0);
+            if (hf + 1 < kRgH) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (k < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        slot = slot == kRgS - 1 ? 0 : slot + 1;
+        slot_next = slot_next == kRgS - 1 ? 0 : slot_next + 1;
+    }
+    vm_wait<0>();   // the empty requests past the last stage
+
+    // 32x32 accumulator layout: lane l, register r holds row 8 (r / 4) + 4 (l / 32) + r % 4, column
+    // l % 32 of its block.  Every residual value is loaded before any output is stored, so the
+    // loads share one memory round trip.
+    const bool full = m0 + kRgBM <= p.M;
+    const int row0 = m0 + wm * 32 + 4 * (lane >> 5);
+    const int col0 = tn * kRgBN + wn * 64 + (lane & 31);
+    if constexpr (EPI == Epilogue::Store) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 8 * (r >> 2) + (r & 3);
+            if (full || row < p.M) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    static_cast<bf16*>(p.out)[(int64_t)row * p.N + col0 + 32 * j] = (bf16)acc[j][r];
+            }
+        }
+    } else {
+        float rv[2][16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = min(row0 + 8 * (r >> 2) + (r & 3), p.M - 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t o = (int64_t)row * p.N + col0 + 32 * j;
+                if constexpr (EPI == Epilogue::ResidToF32)
+                    rv[j][r] = (float)static_cast<const bf16*>(p.resid)[o];
+                else
+                    rv[j][r] = static_cast<const float*>(p.resid)[o];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 8 * (r >> 2) + (r & 3);
+            if (full || row < p.M) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int64_t o = (int64_t)row * p.N + col0 + 32 * j;
+                    if constexpr (EPI == Epilogue::ResidToF32)
+                        static_cast<float*>(p.out)[o] = rv[j][r] + acc[j][r];
+                    else
+                        static_cast<bf16*>(p.out)[o] = (bf16)(rv[j][r] + acc[j][r]);
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ skinny (M <= 64)
 // Weight streaming for decode-sized M: a workgroup owns 16 output columns (16 weight rows, or 16
 // gate and 16 up rows) over the whole K; its NW waves take interleaved 32-k chunks, so the
@@ -1163,6 +1343,15 @@ static hipError_t run_pp_tile(DevGemm p, hipStream_t s) {
 }
 
 template <Epilogue EPI>
+static hipError_t run_ring(DevGemm p, hipStream_t s) {
+    if (!ring_fits(p.M, p.N, p.K)) return hipErrorInvalidValue;
+    p.tiles_m = (p.M + kRgBM - 1) / kRgBM;
+    p.tiles_n = p.N / kRgBN;
+    gemm_bf16_ring_kernel<EPI><<<(unsigned)(p.tiles_m * p.tiles_n), 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <Epilogue EPI>
 static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     // split-K partials, one fp32 slab per K range: 64 x 128 tiles, so the thin products that are
     // split (fewer than 256 tiles of 128 x 128) run two workgroups per CU (0.6B-shaped o_proj and
@@ -1178,6 +1367,9 @@ static hipError_t run_epi(const DevGemm& p, hipStream_t s) {
     // product: 31.5 us against 38-40 us on 768 tiles of 128 x 128).
     if (tiles256 >= 192 && p.N % bn256 == 0 && p.K % 64 == 0) return run_pp_tile<EPI>(p, s);
     if (tiles128 >= 256) return run_tile<EPI, 128, 128, 2, 2>(p, s);
+    // thin products (64 x 128 tiles, deep ring): the residual in the epilogue, K not split
+    if constexpr (!DUAL && EPI != Epilogue::PartialF32)
+        if (ring_fits(p.M, p.N, p.K)) return run_ring<EPI>(p, s);
     if constexpr (DUAL)
         return run_tile<EPI, 64, 128, 2, 2>(p, s);
     else
@@ -1243,7 +1435,7 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
 }
 
 int gemm_bf16_splits(int M, int N, int K) {
-    if (M <= 64 || N % 128 || K % (2 * BK) || K < 512) return 1;
+    if (M <= 64 || N % 128 || K % (2 * BK) || K < 512 || ring_fits(M, N, K)) return 1;
     const long tiles128 = (long)((M + 127) / 128) * (N / 128);
     return tiles128 < 256 ? 2 : 1;
 }
