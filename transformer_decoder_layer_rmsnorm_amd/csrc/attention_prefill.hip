@@ -46,6 +46,8 @@
 //    window start on, so the work grows with T * W instead of T^2.
 //  * Padding and local masks are compiled into a separate instantiation (MASKED), used only when
 //    a call has either; the plain causal kernel carries none of that code.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -80,6 +82,29 @@ __device__ __forceinline__ void pair_xor32(float v, float& a, float& b) {
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
     return __builtin_bit_cast(bf16x4, r);
+}
+
+// Fixed-reference softmax.  When every key of the sequence was normalised by this call (no
+// cached prefix), each score is bounded: q-hat and k-hat are gains times unit-RMS vectors of D
+// features (rotation keeps norms), so |q-hat . k-hat| <= D max|g_q| max|g_k|.  If that bound, in
+// log2 units, is at most 60, the probabilities 2^s need no running maximum: they neither overflow
+// nor underflow in fp32 or bf16, and the softmax, being shift-invariant, is the same up to
+// rounding.  The scale D^-1/2 log2(e) then goes into Q once, so each score costs one exp2, half a
+// conversion and half a row-sum step.  Otherwise (a cached prefix, or large gains) the running
+// maximum is kept.  Returns the wave-uniform decision.
+__device__ __forceinline__ int fixed_reference(const AttnArgs& a, int pos0, int lane, float sl2) {
+    int fixed = 0;
+    if (pos0 == 0 && a.q_norm && a.k_norm) {
+        const bf16* gq = static_cast<const bf16*>(a.q_norm);
+        const bf16* gk = static_cast<const bf16*>(a.k_norm);
+        float mq = fmaxf(fabsf((float)gq[lane] + a.goff), fabsf((float)gq[lane + 64] + a.goff));
+        float mk = fmaxf(fabsf((float)gk[lane] + a.goff), fabsf((float)gk[lane + 64] + a.goff));
+        mq = wave_max(mq);
+        mk = wave_max(mk);
+        // 1.05: room for the bf16 rounding of q-hat, k-hat and the scaled Q
+        fixed = __builtin_amdgcn_readfirstlane((int)(mq * mk * (float)HD * sl2 * 1.05f <= 60.f));
+    }
+    return fixed;
 }
 
 template <int HPW, int KS, bool MASKED>
@@ -160,6 +185,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + (2 * s + (lane >> 5)) * 8);
     }
+    // fixed-reference softmax (see fixed_reference): no running maximum, Q pre-scaled; only in
+    // the split-tile form (KS = 2), whose waves have the registers for a second loop body
+    const int fixed = KS == 2 ? fixed_reference(a, pos0, lane, sl2) : 0;
+    if (fixed) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[s][e] = (bf16)((float)qf[s][e] * sl2);
+    }
     // Buffer descriptors over keys 0 .. kv_len-1 of this (sequence, KV head).
     const int64_t kv_base = ((int64_t)b * a.Hkv + kvh) * a.cap * HD;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -203,7 +237,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    float m_run = -1e30f, l_run = 0.f;
+    float m_run = fixed ? 0.f : -1e30f, l_run = 0.f;   // with the fixed reference the maximum stays 0
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
     auto s_tile = [&](int t, f32x16 (&sacc)[NKB], bool (&live)[NKB]) {
@@ -226,7 +260,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
             }
         }
     };
-    auto softmax_pv = [&](int t, f32x16 (&sacc)[NKB], const bool (&live)[NKB]) {
+    auto softmax_pv = [&](int t, f32x16 (&sacc)[NKB], const bool (&live)[NKB], auto fx) __attribute__((always_inline)) {
+        constexpr bool FX = decltype(fx)::value;
         const int k0 = tidx(t) * KT;
         if (k0 + KT - 1 > wave_first ||
             (MASKED && ((k0 < pad_hi && k0 + KT > pad_lo) || (win > 0 && k0 <= wave_last - win)))) {
@@ -244,25 +279,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
                 }
             }
         }
-        float mt = -INFINITY;
+        if constexpr (!FX) {
+            float mt = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NKB; ++i)
+            for (int i = 0; i < NKB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[i][r]);
-        {
-            float m0v, m1v;
-            pair_xor32(mt, m0v, m1v);
-            mt = fmaxf(m0v, m1v) * sl2;
-        }
-        if (__any(mt > m_run + 8.f)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float corr = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= corr;
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[i][r]);
+            {
+                float m0v, m1v;
+                pair_xor32(mt, m0v, m1v);
+                mt = fmaxf(m0v, m1v) * sl2;
+            }
+            if (__any(mt > m_run + 8.f)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float corr = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= corr;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+                    for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+            }
         }
         bf16x8 pf[NKB][2];
 #pragma unroll
@@ -270,7 +307,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) pf[i][hf][j] = (bf16)fast_exp2(fmaf(sacc[i][8 * hf + j], sl2, -m_run));
+                for (int j = 0; j < 8; ++j)
+                    pf[i][hf][j] = (bf16)fast_exp2(FX ? sacc[i][8 * hf + j] : fmaf(sacc[i][8 * hf + j], sl2, -m_run));
 #pragma unroll
                 for (int j = 0; j < 8; j += 2) {
                     const bf16x2 pp = {pf[i][hf][j], pf[i][hf][j + 1]};
@@ -296,11 +334,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
         }
     };
     // one pipelined step: S of tile t+1 goes out before tile t's softmax and PV
-    auto step = [&](int t, f32x16 (&cur)[NKB], const bool (&lcur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB]) {
+    auto step = [&](int t, f32x16 (&cur)[NKB], const bool (&lcur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB],
+                    auto fx) __attribute__((always_inline)) {
         if (t + 2 < nvis) load_k(t + 2);
         if (t + 1 < nvis) load_v(t + 1);
         if (t + 1 < nvis) s_tile(t + 1, nxt, lnxt);
-        softmax_pv(t, cur, lcur);
+        softmax_pv(t, cur, lcur, fx);
         if (t + 2 < nvis) store_k(t & 1);
         if (t + 1 < nvis) store_v((t + 1) & 1);
         __syncthreads();
@@ -312,28 +351,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     // instructions and one K fragment read, while the matrix core works through the MFMA), and the
     // PV MFMAs with their V fragment reads.  The global loads and LDS stores are unconditional (a
     // clamped tile index): past the last tile they refill a slot no later step reads.
-    auto fast_step = [&](int t, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB]) {
+    auto fast_step = [&](int t, f32x16 (&cur)[NKB], f32x16 (&nxt)[NKB], bool (&lnxt)[NKB], auto fx)
+        __attribute__((always_inline)) {
+        constexpr bool FX = decltype(fx)::value;
         load_k(min(t + 2, nvis - 1));
         load_v(min(t + 1, nvis - 1));
-        float mt = -INFINITY;
+        if constexpr (!FX) {
+            float mt = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NKB; ++i)
+            for (int i = 0; i < NKB; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, cur[i][r]);
-        {
-            float m0v, m1v;
-            pair_xor32(mt, m0v, m1v);
-            mt = fmaxf(m0v, m1v) * sl2;
-        }
-        if (__any(mt > m_run + 8.f)) {
-            const float m_new = fmaxf(m_run, mt);
-            const float corr = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= corr;
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, cur[i][r]);
+            {
+                float m0v, m1v;
+                pair_xor32(mt, m0v, m1v);
+                mt = fmaxf(m0v, m1v) * sl2;
+            }
+            if (__any(mt > m_run + 8.f)) {
+                const float m_new = fmaxf(m_run, mt);
+                const float corr = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= corr;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+                    for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // scores of tile t+1
@@ -357,7 +400,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) pf[i][hf][j] = (bf16)fast_exp2(fmaf(cur[i][8 * hf + j], sl2, -m_run));
+                for (int j = 0; j < 8; ++j)
+                    pf[i][hf][j] = (bf16)fast_exp2(FX ? cur[i][8 * hf + j] : fmaf(cur[i][8 * hf + j], sl2, -m_run));
 #pragma unroll
                 for (int j = 0; j < 8; j += 2) {
                     const bf16x2 pp = {pf[i][hf][j], pf[i][hf][j + 1]};
@@ -381,14 +425,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
                 }
             }
         }
-        // issue order: K reads ahead, then per score MFMA six VALU instructions of the softmax and
-        // one more K read; then the PV MFMAs, two V reads ahead of each
+        // issue order: K reads ahead, then per score MFMA six VALU instructions of the softmax (four
+        // with the fixed reference) and one more K read; then the PV MFMAs, two V reads ahead of each
         constexpr int NS = 8 * NKB;   // score MFMAs (= K fragment reads)
+        constexpr int NV = FX ? 4 : 6;
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int k = 0; k < NS; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
             if (k + 4 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -417,21 +462,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fl
     bool la[NKB], lb[NKB];
     s_tile(0, sa, la);
     int t = 0;
-    if constexpr (!MASKED) {
-        // Tiles wholly at or below the first query of the workgroup need no mask and have every key
-        // block live; all but the last (whose step would have no next tile to score) run the
-        // branch-free step, in pairs so the two score buffers alternate statically.
-        const int nfull = (pos0 + q0 + 1) / KT;
-        const int nfast = min(nfull, nvis - 1) & ~1;
-        for (; t < nfast; t += 2) {
-            fast_step(t, sa, sb, lb);
-            fast_step(t + 1, sb, sa, la);
+    // the tile loop, instantiated with and without the running maximum
+    auto run = [&](auto fx) __attribute__((always_inline)) {
+        if constexpr (!MASKED) {
+            // Tiles wholly at or below the first query of the workgroup need no mask and have every
+            // key block live; all but the last (whose step would have no next tile to score) run the
+            // branch-free step, in pairs so the two score buffers alternate statically.
+            const int nfull = (pos0 + q0 + 1) / KT;
+            const int nfast = min(nfull, nvis - 1) & ~1;
+            for (; t < nfast; t += 2) {
+                fast_step(t, sa, sb, lb, fx);
+                fast_step(t + 1, sb, sa, la, fx);
+            }
         }
-    }
-    for (; t < nvis; t += 2) {
-        step(t, sa, la, sb, lb);
-        if (t + 1 >= nvis) break;
-        step(t + 1, sb, lb, sa, la);
+        for (; t < nvis; t += 2) {
+            step(t, sa, la, sb, lb, fx);
+            if (t + 1 >= nvis) break;
+            step(t + 1, sb, lb, sa, la, fx);
+        }
+    };
+    if constexpr (KS == 2) {
+        if (fixed)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
+    } else {
+        run(std::false_type{});
     }
 
     if constexpr (KS == 2) {
@@ -548,25 +604,9 @@ __global__ __launch_bounds__(512) void flash_prefill_pp_kernel(AttnArgs a, float
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + (2 * s + (lane >> 5)) * 8);
     }
-    // Fixed-reference softmax.  When every key of the sequence was normalised by this call (no
-    // cached prefix), each score is bounded: q-hat and k-hat are gains times unit-RMS vectors of D
-    // features (rotation keeps norms), so |q-hat . k-hat| <= D max|g_q| max|g_k|.  If that bound,
-    // in log2 units, is at most 60, the probabilities 2^s need no running maximum: they neither
-    // overflow nor underflow in fp32 or bf16, and the softmax, being shift-invariant, is the same
-    // up to rounding.  The scale D^-1/2 log2(e) then goes into Q once, so each score costs one
-    // exp2, half a conversion and half a row-sum step: the vector phase shrinks to well under the
-    // matrix phase.  Otherwise (a cached prefix, or large gains) the running maximum is kept.
-    int fixed = 0;
-    if (pos0 == 0 && a.q_norm && a.k_norm) {
-        const bf16* gq = static_cast<const bf16*>(a.q_norm);
-        const bf16* gk = static_cast<const bf16*>(a.k_norm);
-        float mq = fmaxf(fabsf((float)gq[lane] + a.goff), fabsf((float)gq[lane + 64] + a.goff));
-        float mk = fmaxf(fabsf((float)gk[lane] + a.goff), fabsf((float)gk[lane + 64] + a.goff));
-        mq = wave_max(mq);
-        mk = wave_max(mk);
-        // 1.05: room for the bf16 rounding of q-hat, k-hat and the scaled Q
-        fixed = __builtin_amdgcn_readfirstlane((int)(mq * mk * (float)HD * sl2 * 1.05f <= 60.f));
-    }
+    // fixed-reference softmax (see fixed_reference): the vector phase shrinks to well under the
+    // matrix phase
+    const int fixed = fixed_reference(a, pos0, lane, sl2);
     if (fixed) {
 #pragma unroll
         for (int s = 0; s < 8; ++s)
