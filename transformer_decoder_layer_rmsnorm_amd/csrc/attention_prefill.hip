@@ -65,7 +65,6 @@ constexpr int NT = 256;               // threads per workgroup (4 waves)
 constexpr int CH = (KT * HD / 8) / NT;  // 16-byte chunks of K (and of V) staged per thread
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 // v of lane l and of lane l ^ 32, in (a, b): v_permlane32_swap exchanges the upper 32 lanes of its

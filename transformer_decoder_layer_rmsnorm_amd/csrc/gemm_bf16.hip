@@ -92,6 +92,54 @@ template <Epilogue EPI, int BN, int TM, int TN, int FM, int FN>
 __device__ __forceinline__ void write_tile(const DevGemm& p, const f32x16 (&acc)[FM][FN], int m0, int tn, int wm,
                                            int wn, int lane) {
     constexpr bool DUAL = (EPI == Epilogue::SwiGLU);
+    if constexpr (DUAL) {
+        // Every row of the wave in range (all but a ragged last tile): no per-row branch, so the
+        // exponentials and reciprocals of all the wave's outputs are one straight-line block the
+        // compiler interleaves, instead of short dependent chains behind an exec-mask branch each.
+        if (m0 + wm * TM + TM <= p.M) {
+            bf16* out = static_cast<bf16*>(p.out) + tn * (BN / 2) + (wn * TN) / 2 + (lane & 31);
+            constexpr int NJ = FN / 2;   // outputs per row and lane
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    // four rows at a time: their 4 NJ exponentials, then the reciprocals, then the
+                    // products and stores (silu(g) u = g u / (1 + e^-g))
+                    float e[4][NJ];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                        for (int jj = 0; jj < NJ; ++jj) e[rr][jj] = __expf(-acc[i][2 * jj][4 * rq + rr]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                        for (int jj = 0; jj < NJ; ++jj) e[rr][jj] = __builtin_amdgcn_rcpf(1.0f + e[rr][jj]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int row = m0 + wm * TM + i * 32 + 8 * rq + 4 * (lane >> 5) + rr;
+                        const int r = 4 * rq + rr;
+                        if constexpr (NJ == 2) {
+                            // lanes 2k and 2k + 1 hold adjacent columns of the row: they swap one
+                            // output so that each stores two adjacent ones in 4 bytes (the even
+                            // lane its column and the next, the odd lane columns 31 + its own)
+                            const float o0 = acc[i][0][r] * acc[i][1][r] * e[rr][0];
+                            const float o1 = acc[i][2][r] * acc[i][3][r] * e[rr][1];
+                            const bool odd = lane & 1;
+                            const float recv = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                0, __builtin_bit_cast(int, odd ? o0 : o1), 0xB1, 0xf, 0xf, false));
+                            const bf16x2 pk = {(bf16)(odd ? recv : o0), (bf16)(odd ? o1 : recv)};
+                            *reinterpret_cast<bf16x2*>(out + (int64_t)row * p.N + (odd ? 31 : 0)) = pk;
+                        } else {
+#pragma unroll
+                            for (int jj = 0; jj < NJ; ++jj)
+                                out[(int64_t)row * p.N + jj * 32] =
+                                    (bf16)(acc[i][2 * jj][r] * acc[i][2 * jj + 1][r] * e[rr][jj]);
+                        }
+                    }
+                }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
