@@ -149,6 +149,19 @@ def test_workspace_size_and_layout(layer):
     assert L.qwen3_layer_workspace_size(layer, 0, 5, 5, ctypes.byref(n)) == nat.QWEN3_ERR_INVALID_ARGUMENT
 
 
+def test_workspace_split_k_slabs_only_for_few_output_tiles(layer):
+    """0.6B-shaped o_proj and down (N = 1024, K = 2048 and 3072): at 2048 tokens the deep-ring GEMM
+    (at least 128 tiles of 64 x 128) covers them with K unsplit, so the layout holds no fp32 partial
+    slabs; at 300 tokens (40 such tiles) K is split in two and the [2, M, H] slabs are there."""
+    L = nat.lib()
+    for t, slabs in ((2048, 0), (300, 2)):
+        lay = nat.WorkspaceLayout()
+        assert L.qwen3_layer_workspace_layout(layer, 1, t, t, ctypes.byref(lay)) == nat.QWEN3_OK
+        region = lay.lens - lay.part_gemm
+        assert region >= slabs * t * 1024 * 4
+        assert region < (slabs * t * 1024 * 4) + 256, (t, region)
+
+
 def prefill(layer, b=1, t=16, cap=16, ws_bytes=1 << 30, x=FAKE, kc=FAKE):
     return nat.lib().qwen3_layer_prefill(layer, x, FAKE, b, t, kc, FAKE, cap, FAKE, ws_bytes, None)
 
