@@ -79,11 +79,27 @@ def test_qwen3_8b_layer_prefill_ragged_tail_rows():
     assert_bf16_parity(to_np(y)[0, ts], ref, f"y at {len(ts)} rows incl. the 40-row tail")
 
 
+def test_qwen3_8b_layer_prefill_thin_every_element():
+    """8B shapes at T = 300 (four whole 64-row tiles plus a 44-row tail, 160 tiles of 64 x 128):
+    o_proj (K = 4096) and down (K = 12288, 96 stages of the ring) take the deep-ring GEMM with
+    the residual in its epilogue; every element of y and of the caches against the oracle."""
+    wl = si.WORKLOADS["qwen3-8b-layer-prefill"]
+    cfg = wl.cfg
+    t_len = 300
+    log(f"8B-shaped layer: B1 T{t_len}")
+    gl = GpuLayer.seeded(cfg, seed=wl.seed + 3)
+    x = si.layer_input(cfg, 1, t_len, seed=wl.seed + 3)
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg))
+    ref = oracle.layer_prefill(x, gl.w_np, cfg)
+    assert_bf16_parity(to_np(y), ref["y"], "y, every element")
+    assert_bf16_parity(to_np(kc), ref["khat"], "k cache, every element")
+
+
 def test_qwen3_0p6b_layer_prefill_ragged_tail_rows():
     """0.6B shapes at T = 2088 (32 whole 64-row tiles plus a 40-row tail): o_proj and down take
-    the split-K 64 x 128 tiles, gate/up the 256 x 256 ping-pong tiles, QKV the fused 256 x 128
-    ping-pong kernel, all with a partial last row tile; rows in and around the tail are
-    checked."""
+    the deep-ring 64 x 128 tiles with the residual in their epilogue, gate/up the 256 x 256
+    ping-pong tiles, QKV the fused 256 x 128 ping-pong kernel, all with a partial last row tile;
+    rows in and around the tail are checked."""
     wl = si.WORKLOADS["qwen3-0.6b-layer-prefill"]
     cfg = wl.cfg
     t_len = 2088
