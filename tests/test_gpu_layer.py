@@ -234,6 +234,36 @@ def test_bf16_attention_two_group_large_gains():
     check_prefill_stages_full(gl, x, y, kc, vc, ws, "6x gains")
 
 
+@pytest.mark.parametrize("shape", ["small", "8b"])
+def test_bf16_single_token_attends_only_itself(shape):
+    """The degenerate sequence of one token: a prefill of T = 1 and a decode step on empty caches
+    (length 0).  The softmax over a single key is exactly 1, so the attention output must be that
+    token's value row, bit for bit after the bf16 rounding (the normalisation divides p v by p);
+    the layer outputs are compared with the oracle's prefill of the same token."""
+    cfg = small_bf16_cfg(hq=8, hkv=2) if shape == "small" else si.WORKLOADS["qwen3-8b-layer-prefill"].cfg
+    b = 3
+    log(f"bf16 single token, {shape}, B{b}")
+    gl = GpuLayer.seeded(cfg, seed=11)
+    x = si.layer_input(cfg, b, 1, seed=12)
+    ref = oracle.layer_prefill(x, gl.w_np, cfg)["y"]
+    hq, hkv, d = cfg.num_attention_heads, cfg.num_key_value_heads, cfg.head_dim
+    g = hq // hkv
+    # prefill of T = 1
+    y, kc, vc, ws = gl.prefill(to_dev(x, cfg), cap=4)
+    it = gl.intermediates(ws, b, 1, 4)
+    v0 = to_np(vc)[:, :, 0, :]                                   # [B, Hkv, D]
+    want = np.repeat(v0, g, axis=1).reshape(b, 1, hq * d)        # head h reads KV head h // g
+    assert np.array_equal(it["attn"], want), "prefill T=1: attention output is the value row"
+    assert_bf16_parity(to_np(y), ref, "prefill T=1, y")
+    # decode on empty caches: the token is written at slot 0 and attends only itself
+    kc2, vc2 = gl.alloc_cache(b, 4)
+    yd, wsd = gl.decode(to_dev(x, cfg), [0] * b, kc2, vc2)
+    itd = gl.intermediates(wsd, b, 1, 4)
+    assert np.array_equal(to_np(vc2)[:, :, 0, :], v0), "decode writes the same value row"
+    assert np.array_equal(itd["attn"], want), "decode on empty caches: attention output is the value row"
+    assert_bf16_parity(to_np(yd), ref, "decode on empty caches, y")
+
+
 def test_bf16_causality_bit_exact():
     cfg = small_bf16_cfg()
     gl = GpuLayer.seeded(cfg, seed=9)
