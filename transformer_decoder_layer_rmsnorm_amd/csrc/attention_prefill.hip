@@ -768,29 +768,33 @@ __global__ __launch_bounds__(512) void flash_prefill_pp_kernel(AttnArgs a, float
     };
     // vector phase of tile t (register set t & 1): this group's staging, then the softmax of tile t.
     // Group 0 writes V(t) and requests V(t + 2); group 1 writes K(t + 2) (slot t & 1) and requests
-    // K(t + 4).
+    // K(t + 4).  Every vector phase requests its tile, past the last one the last tile again
+    // (loaded, never stored): with the same requests on every path the compiler sees that the
+    // set being stored is the older one and waits for it alone (vmcnt(CH)), not also for the
+    // other set requested only two phases before.
     auto vector_phase = [&](int t, int4v (&r)[CH]) {
         if (grp == 0) {
-            if (t >= 0 && t < n) {
-                store_v(r, t & 1);
-                if (t + 2 < n) load_tile(r, vrs, t + 2);
-            }
-        } else if (t + 2 < n) {
-            store_k(r, t & 1);
-            if (t + 4 < n) load_tile(r, krs, t + 4);
+            if (t >= 0 && t < n) store_v(r, t & 1);
+            load_tile(r, vrs, min(t + 2, n - 1));
+        } else {
+            if (t + 2 < n) store_k(r, t & 1);
+            load_tile(r, krs, min(t + 4, n - 1));
         }
         softmax_phase(t);
     };
 
-    // prologue: K(0) in LDS; group 0 holds V(0), V(1), group 1 K(1), K(2) in its registers
+    // prologue: K(0) in LDS; group 0 holds V(0), V(1), group 1 K(1), K(2) in its registers (a
+    // tile index past the last one loads the last tile).  In both groups set 1 is requested last,
+    // as at the end of every loop step, so the compiler's wait before each set's LDS store is the
+    // same exact count on every path into the loop.
     if (grp == 1) {
         load_tile(stg[0], krs, 0);
         store_k(stg[0], 0);
-        if (n > 1) load_tile(stg[1], krs, 1);
-        if (n > 2) load_tile(stg[0], krs, 2);
+        load_tile(stg[0], krs, min(2, n - 1));
+        load_tile(stg[1], krs, min(1, n - 1));
     } else {
         load_tile(stg[0], vrs, 0);
-        if (n > 1) load_tile(stg[1], vrs, 1);
+        load_tile(stg[1], vrs, min(1, n - 1));
     }
     lds_barrier();
     // Every wave runs matrix(k), vector(k) in turn; group 1 starts one phase later (its vector
@@ -801,19 +805,26 @@ __global__ __launch_bounds__(512) void flash_prefill_pp_kernel(AttnArgs a, float
         vector_phase(-1, stg[1]);
         lds_barrier();
     }
-    for (int k = 0; k <= n; k += 2) {
+    // whole pairs in the loop (no conditional requests in its body), the odd last step after it
+    int k = 0;
+    for (; k + 1 <= n; k += 2) {
         matrix_phase(k);
         lds_barrier();
         vector_phase(k, stg[0]);
         lds_barrier();
-        if (k + 1 <= n) {
-            matrix_phase(k + 1);
-            lds_barrier();
-            vector_phase(k + 1, stg[1]);
-            lds_barrier();
-        }
+        matrix_phase(k + 1);
+        lds_barrier();
+        vector_phase(k + 1, stg[1]);
+        lds_barrier();
+    }
+    if (k <= n) {
+        matrix_phase(k);
+        lds_barrier();
+        vector_phase(k, stg[0]);
+        lds_barrier();
     }
     if (grp == 0) lds_barrier();
+    __builtin_amdgcn_s_waitcnt(0);   // the requests past the last tile
 
     // normalise and store: lane holds d = db*32 + 8(r/4) + 4(lane/32) + r%4 of its query
     float l0v, l1v;
