@@ -79,20 +79,22 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TX* __restrict__ x, 
 }
 
 // Input RMSNorm (bf16) plus the RoPE table row of each token: lane i of the row's wave forms the
-// angle of frequency i (see RopeTable).  Rows up to 4096 wide stay in registers between the
-// reduction and the output; wider rows (WIDE) are read twice.
-template <bool WIDE>
+// angle of frequency i (see RopeTable).  Rows up to 64 NC wide stay in registers between the
+// reduction and the output; wider rows (NC = 0) are read twice.  EARLY_G as in rmsnorm_kernel.
+template <int NC, bool EARLY_G>
 __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restrict__ x, const bf16* __restrict__ g,
                                                            bf16* __restrict__ y, int64_t rows, int width, float eps,
                                                            float goff, RopeTable rope) {
-    constexpr int MAXC = WIDE ? 1 : 8;
+    constexpr bool WIDE = NC == 0;
+    constexpr int MAXC = WIDE ? 1 : NC;
+    static_assert(!(WIDE && EARLY_G), "wide rows read the gains in the output pass");
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const bf16* xr = x + row * width;
     bf16* yr = y + row * width;
     const int nchunk = width >> 3;
-    float v[MAXC][8];
+    float v[MAXC][8], gv0[EARLY_G ? MAXC : 1][8];
     float ss = 0.f;
     if constexpr (WIDE) {
         for (int c = lane; c < nchunk; c += kWave) {
@@ -106,6 +108,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
             const int c = lane + j * kWave;
             if (c < nchunk) {
                 load8(xr + c * 8, v[j]);
+                if constexpr (EARLY_G) load8(g + c * 8, gv0[j]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) ss = fmaf(v[j][i], v[j][i], ss);
             }
@@ -137,7 +140,12 @@ __global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const bf16* __restric
             const int c = lane + j * kWave;
             if (c < nchunk) {
                 float gv[8], o[8];
-                load8(g + c * 8, gv);
+                if constexpr (EARLY_G) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) gv[i] = gv0[j][i];
+                } else {
+                    load8(g + c * 8, gv);
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = (goff + gv[i]) * (v[j][i] * rstd);
                 store8(yr + c * 8, o);
@@ -151,12 +159,18 @@ hipError_t launch_rmsnorm_rope(const void* x, const void* g, void* y, int64_t ro
     if (rows <= 0) return hipSuccess;
     if ((width & 7) || rope.T <= 0 || !rope.cs || !rope.slot) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((rows + 3) / 4);
-    if (width <= 8 * 8 * kWave)
-        rmsnorm_rope_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g),
-                                                        static_cast<bf16*>(y), rows, width, eps, goff, rope);
+#define Q3_RMS_ROPE(NC, EG)                                                                                      \
+    rmsnorm_rope_kernel<NC, EG><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g), \
+                                                    static_cast<bf16*>(y), rows, width, eps, goff, rope)
+    // rows up to 1024 wide: two chunks per lane, the gains requested with the row (one memory round
+    // trip per row instead of two, and few enough registers for full occupancy)
+    if (width <= 2 * 8 * kWave)
+        Q3_RMS_ROPE(2, true);
+    else if (width <= 8 * 8 * kWave)
+        Q3_RMS_ROPE(8, false);
     else
-        rmsnorm_rope_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16*>(x), static_cast<const bf16*>(g),
-                                                       static_cast<bf16*>(y), rows, width, eps, goff, rope);
+        Q3_RMS_ROPE(0, false);
+#undef Q3_RMS_ROPE
     return hipGetLastError();
 }
 
@@ -164,7 +178,10 @@ template <typename TX, typename TY>
 static hipError_t launch_typed(const void* x, const void* g, void* y, int64_t rows, int width, float eps,
                                float goff, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
-    if (rows <= 1024)   // fewer rows than one per wave slot of the chip: latency-bound
+    if (width <= 2 * 8 * kWave)   // two chunks per lane: the gains with the row, one round trip
+        rmsnorm_kernel<TX, TY, 2, true><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
+                                                             static_cast<TY*>(y), rows, width, eps, goff);
+    else if (rows <= 1024)   // fewer rows than one per wave slot of the chip: latency-bound
         rmsnorm_kernel<TX, TY, 8, true><<<grid, 256, 0, s>>>(static_cast<const TX*>(x), static_cast<const TY*>(g),
                                                              static_cast<TY*>(y), rows, width, eps, goff);
     else
