@@ -766,13 +766,18 @@ __global__ __launch_bounds__(512) void flash_prefill_pp_kernel(AttnArgs a, float
                     acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
                 }
     };
-    // vector phase of tile t (register set t & 1): this group's staging, then the softmax of tile t.
+    // vector phase of tile t (register set t & 1): this group's staging and the softmax of tile t.
     // Group 0 writes V(t) and requests V(t + 2); group 1 writes K(t + 2) (slot t & 1) and requests
     // K(t + 4).  Every vector phase requests its tile, past the last one the last tile again
     // (loaded, never stored): with the same requests on every path the compiler sees that the
     // set being stored is the older one and waits for it alone (vmcnt(CH)), not also for the
     // other set requested only two phases before.
-    auto vector_phase = [&](int t, int4v (&r)[CH]) {
+    // With two heads per wave the staging goes after the softmax, pinned there: the LDS stores then
+    // meet the other group's fragment reads near their end instead of delaying this group's
+    // exponentials (stack attention 258 -> 254.5 us); with four heads per wave, whose vector phase
+    // is longer, the earlier request of the next tile matters more (8B attention 486 us before the
+    // softmax, 499 after).
+    auto staging = [&](int t, int4v (&r)[CH]) {
         if (grp == 0) {
             if (t >= 0 && t < n) store_v(r, t & 1);
             load_tile(r, vrs, min(t + 2, n - 1));
@@ -780,7 +785,16 @@ __global__ __launch_bounds__(512) void flash_prefill_pp_kernel(AttnArgs a, float
             if (t + 2 < n) store_k(r, t & 1);
             load_tile(r, krs, min(t + 4, n - 1));
         }
-        softmax_phase(t);
+    };
+    auto vector_phase = [&](int t, int4v (&r)[CH]) {
+        if constexpr (HPW == 2) {
+            softmax_phase(t);
+            __builtin_amdgcn_sched_barrier(0);
+            staging(t, r);
+        } else {
+            staging(t, r);
+            softmax_phase(t);
+        }
     };
 
     // prologue: K(0) in LDS; group 0 holds V(0), V(1), group 1 K(1), K(2) in its registers (a
