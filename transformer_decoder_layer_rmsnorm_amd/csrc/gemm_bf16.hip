@@ -97,7 +97,15 @@ __device__ __forceinline__ void write_tile(const DevGemm& p, const f32x16 (&acc)
         // exponentials and reciprocals of all the wave's outputs are one straight-line block the
         // compiler interleaves, instead of short dependent chains behind an exec-mask branch each.
         if (m0 + wm * TM + TM <= p.M) {
-            bf16* out = static_cast<bf16*>(p.out) + tn * (BN / 2) + (wn * TN) / 2 + (lane & 31);
+            // the wave's rows from one uniform base: each store address is that base plus a 32-bit
+            // lane offset plus a uniform row offset (no 64-bit arithmetic per row); TM rows of N
+            // bf16 stay far below 4 GiB
+            char* base = reinterpret_cast<char*>(static_cast<bf16*>(p.out) + (int64_t)(m0 + wm * TM) * p.N +
+                                                 tn * (BN / 2) + (wn * TN) / 2);
+            const unsigned lane_off = (unsigned)(4 * (lane >> 5) * p.N + (lane & 31) + ((lane & 1) ? 31 : 0)) * 2u;
+            // bytes of {partner's word, own word}: even lanes (own low, partner low), odd lanes
+            // (partner high, own high)
+            const unsigned pair_sel = (lane & 1) ? 0x03020706u : 0x05040100u;
             constexpr int NJ = FN / 2;   // outputs per row and lane
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -116,23 +124,24 @@ __device__ __forceinline__ void write_tile(const DevGemm& p, const f32x16 (&acc)
                         for (int jj = 0; jj < NJ; ++jj) e[rr][jj] = __builtin_amdgcn_rcpf(1.0f + e[rr][jj]);
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        const int row = m0 + wm * TM + i * 32 + 8 * rq + 4 * (lane >> 5) + rr;
                         const int r = 4 * rq + rr;
+                        const unsigned row_off = (unsigned)((i * 32 + 8 * rq + rr) * p.N) * 2u;
                         if constexpr (NJ == 2) {
-                            // lanes 2k and 2k + 1 hold adjacent columns of the row: they swap one
-                            // output so that each stores two adjacent ones in 4 bytes (the even
-                            // lane its column and the next, the odd lane columns 31 + its own)
-                            const float o0 = acc[i][0][r] * acc[i][1][r] * e[rr][0];
-                            const float o1 = acc[i][2][r] * acc[i][3][r] * e[rr][1];
-                            const bool odd = lane & 1;
-                            const float recv = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                0, __builtin_bit_cast(int, odd ? o0 : o1), 0xB1, 0xf, 0xf, false));
-                            const bf16x2 pk = {(bf16)(odd ? recv : o0), (bf16)(odd ? o1 : recv)};
-                            *reinterpret_cast<bf16x2*>(out + (int64_t)row * p.N + (odd ? 31 : 0)) = pk;
+                            // lanes 2k and 2k + 1 hold adjacent columns of the row: each packs its
+                            // two outputs (columns c and c + 32), the pair swaps the packed words,
+                            // and a byte permute keeps two adjacent outputs per lane for one 4-byte
+                            // store (the even lane its column and the next, the odd lane columns
+                            // 31 + its own)
+                            const bf16x2 own = {(bf16)(acc[i][0][r] * acc[i][1][r] * e[rr][0]),
+                                                (bf16)(acc[i][2][r] * acc[i][3][r] * e[rr][1])};
+                            const unsigned pw = __builtin_bit_cast(unsigned, own);
+                            const unsigned qw = (unsigned)__builtin_amdgcn_mov_dpp((int)pw, 0xB1, 0xf, 0xf, false);
+                            *reinterpret_cast<unsigned*>(base + (lane_off + row_off)) = __builtin_amdgcn_perm(qw, pw, pair_sel);
                         } else {
+                            const unsigned own = lane_off - ((lane & 1) ? 62u : 0u);   // this lane's column
 #pragma unroll
                             for (int jj = 0; jj < NJ; ++jj)
-                                out[(int64_t)row * p.N + jj * 32] =
+                                *reinterpret_cast<bf16*>(base + (own + row_off + jj * 64)) =
                                     (bf16)(acc[i][2 * jj][r] * acc[i][2 * jj + 1][r] * e[rr][jj]);
                         }
                     }
