@@ -309,6 +309,20 @@ def bench_stack(torch, si, nat, wl, steps, warmup):
             "kernels": kernel_table(avg, flops)}
 
 
+def plain_read_reference(torch, tensors, steps, warmup):
+    """A same-box reference for the decode attention's bandwidth: one plain streaming read of
+    the same bytes, torch.sum over rows of 4096 bf16 values into fp32 (one small output per row),
+    timed like a step.  Returns ms per pass over all the tensors."""
+    views = [t.view(-1, 4096) for t in tensors]
+
+    def run():
+        for v in views:
+            torch.sum(v, dim=1, dtype=torch.float32)
+
+    ms, _ = time_steps(torch, run, steps, warmup)
+    return ms
+
+
 def bench_decode(torch, si, nat, wl, steps, warmup, w_np=None):
     cfg = wl.cfg
     dt = torch.bfloat16
@@ -325,8 +339,10 @@ def bench_decode(torch, si, nat, wl, steps, warmup, w_np=None):
     step = lambda: run.layer.decode(run.x, run.y, lens, run.kc, run.vc, run.ws)
     ms, med = time_steps(torch, step, steps, warmup)
     avg = profile_steps(torch, [run.layer], step, steps)
+    read_ms = plain_read_reference(torch, [run.kc, run.vc], steps, warmup)
     run.layer.close()
     kv = decode_attention_bytes(cfg, wl.batch, n)
+    read_gbs = kv / (read_ms * 1e-3) / 1e9
     attn_ms = avg["attention_decode_split"] + avg["attention_decode_combine"]
     gbs = kv / (attn_ms * 1e-3) / 1e9
     split_gbs = kv / (avg["attention_decode_split"] * 1e-3) / 1e9
@@ -340,7 +356,14 @@ def bench_decode(torch, si, nat, wl, steps, warmup, w_np=None):
                          "avg_ms": round(attn_ms, 5), "bytes_per_launch": kv,
                          "split_kernel_only": {"avg_ms": round(avg["attention_decode_split"], 5),
                                                "achieved": round(split_gbs, 1),
-                                               "frac": round(split_gbs / PEAK_HBM_GBS, 4)}},
+                                               "frac": round(split_gbs / PEAK_HBM_GBS, 4)},
+                         # the same K/V bytes read by a plain streaming reduction on this machine:
+                         # what the memory system delivers to a simple read, for context
+                         "plain_read_reference": {"op": "torch.sum(cache.view(-1, 4096), dim=1, dtype=float32) "
+                                                        "over the K and V caches",
+                                                  "ms": round(read_ms, 5), "gbs": round(read_gbs, 1),
+                                                  "frac_of_peak": round(read_gbs / PEAK_HBM_GBS, 4),
+                                                  "attention_frac_of_reference": round(gbs / read_gbs, 4)}},
             "layer_bytes": layer_bytes,
             "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
             "layer_frac_of_hbm_peak": round(layer_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
