@@ -674,6 +674,28 @@ def summarize_rocprof(db, mode):
                          f"{avg(a.get('SQ_INSTS_VALU', [])) / mf:.2f} | {avg(a.get('SQ_INSTS_VALU_TRANS_F32', [])) / mf:.2f} | "
                          f"{avg(a.get('SQ_INSTS_LDS', [])) / mf:.2f} | {util:.1f} | {co:.1f} |")
         return "\n".join(lines)
+    if mode == "lds":
+        # LDS use of each kernel: SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT are cycles summed over
+        # the CUs, so divided by 256 CUs x one XCD's GRBM_GUI_ACTIVE they are the share of CU
+        # cycles the LDS was busy or stalled on bank conflicts; the *_BANDWIDTH counters count 64-byte
+        # units moved; SQ_WAIT_INST_LDS counts wave-cycles (units of 4) waiting to issue an LDS
+        # instruction, given here per wave slot (8 waves per CU at full occupancy of these kernels)
+        lines.append("| kernel | grid (workgroups) | dispatches | avg us | LDS busy % of CU cycles | bank-conflict "
+                     "stall % | LDS read B/clk/CU | LDS write B/clk/CU | LDS-issue wait % of 8 wave slots |")
+        lines.append("|---|---|---|---|---|---|---|---|---|")
+        for k in sorted(agg, key=lambda k: -avg(agg[k].get("_us", [0])) * len(agg[k].get("_us", [0]))):
+            a = agg[k]
+            gui = avg(a.get("GRBM_GUI_ACTIVE", [])) / XCD_COUNT
+            if not gui or not a.get("SQ_LDS_IDX_ACTIVE") or avg(a["SQ_LDS_IDX_ACTIVE"]) < 0.01 * CU_COUNT * gui:
+                continue
+            cyc = CU_COUNT * gui
+            lines.append(f"| `{k[0]}` | {k[1:]} | {len(a['GRBM_GUI_ACTIVE'])} | {avg(a.get('_us', [])):.2f} | "
+                         f"{100 * avg(a['SQ_LDS_IDX_ACTIVE']) / cyc:.1f} | "
+                         f"{100 * avg(a.get('SQ_LDS_BANK_CONFLICT', [0])) / cyc:.2f} | "
+                         f"{64 * avg(a.get('SQ_INSTS_LDS_LOAD_BANDWIDTH', [0])) / cyc:.1f} | "
+                         f"{64 * avg(a.get('SQ_INSTS_LDS_STORE_BANDWIDTH', [0])) / cyc:.1f} | "
+                         f"{100 * 4 * avg(a.get('SQ_WAIT_INST_LDS', [0])) / (8 * cyc):.1f} |")
+        return "\n".join(lines)
     lines.append("| kernel | grid (workgroups) | dispatches | avg us | MFMA busy % | clock MHz | bf16 MFMA MOPS |")
     lines.append("|---|---|---|---|---|---|---|")
     for k in sorted(agg, key=lambda k: -avg(agg[k].get("_us", [0])) * len(agg[k].get("_us", [0]))):
@@ -704,7 +726,7 @@ def main():
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time torch.matmul (hipBLASLt) on the headline workload's projection shapes")
     ap.add_argument("--summarize-rocprof", metavar="DB", help="print a markdown summary of a rocprofv3 database")
-    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "traffic-json", "mfma", "issue"],
+    ap.add_argument("--mode", default="trace", choices=["trace", "traffic", "traffic-json", "mfma", "issue", "lds"],
                     help="summary kind; traffic modes take the FETCH_SIZE and WRITE_SIZE databases, comma-separated")
     args = ap.parse_args()
     if args.summarize_rocprof:
