@@ -243,10 +243,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeAttnArgs p, flo
 
 // Merge the splits of one (head, sequence).  The global max of the split maxima comes from a
 // block reduction; then, chunk by chunk, the split weights 2^(m_s - m) go to LDS and the 256
-// threads split the (split, feature) pairs so that each keeps several independent loads in
-// flight; the two halves of the block combine through LDS.
+// threads split the (split, feature) pairs: thread (half, d) sums feature d over splits half,
+// half + 2, ... of the chunk, in four independent chains; the two halves combine through LDS.
+// The partial outputs of the first chunk (up to 64 splits: every split of a 64K-key cache) are
+// requested before the maximum is formed, so a call costs one memory round trip, not two.
 constexpr int kCombineThreads = 256;
-constexpr int kSplitChunk = 1024;
+constexpr int kSplitChunk = 64;          // splits per chunk: 32 partial outputs per thread
+constexpr int kPerThread = kSplitChunk / 2;
 
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeAttnArgs p) {
     __shared__ float sW[kSplitChunk];
@@ -259,36 +262,46 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     const int ns = (kv_len + SK - 1) / SK;
     const int64_t row0 = ((int64_t)b * a.Hq + h) * p.splits;
     const float* ml = p.part_ml + row0 * 2;
+    const int d = tid & (HD - 1), half = tid >> 7;
+    const float* po = p.part_o + row0 * HD + d;
+
+    // partial outputs of chunk c0: this thread's splits c0 + half + 2i (zero past the last split)
+    float ov[kPerThread];
+    auto request = [&](int c0) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int sp = c0 + half + 2 * i;
+            ov[i] = sp < ns ? po[(int64_t)sp * HD] : 0.f;
+        }
+    };
+    request(0);
 
     float m = -INFINITY;
-    for (int s = tid; s < ns; s += kCombineThreads) m = fmaxf(m, ml[2 * s]);
+    for (int sp = tid; sp < ns; sp += kCombineThreads) m = fmaxf(m, ml[2 * sp]);
     m = wave_max(m);
     if (lane == 0) sRed[wave] = m;
     __syncthreads();
     m = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
 
-    // thread (half, d) sums splits half, half + 2, ... of each chunk for feature d
-    const int d = tid & (HD - 1), half = tid >> 7;
-    const float* po = p.part_o + row0 * HD + d;
     float l = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
     for (int c0 = 0; c0 < ns; c0 += kSplitChunk) {
         const int n = min(kSplitChunk, ns - c0);
         __syncthreads();                        // previous chunk's weights are no longer read
-        for (int s = tid; s < n; s += kCombineThreads) {
-            const float w = fast_exp2(ml[2 * (c0 + s)] - m);
-            sW[s] = w;
-            l = fmaf(w, ml[2 * (c0 + s) + 1], l);
+        if (tid < n) {
+            const float w = fast_exp2(ml[2 * (c0 + tid)] - m);
+            sW[tid] = w;
+            l = fmaf(w, ml[2 * (c0 + tid) + 1], l);
         }
+        if (tid >= n && tid < kSplitChunk) sW[tid] = 0.f;   // splits past the last: weight 0
         __syncthreads();
-        const float* pc = po + (int64_t)c0 * HD;
-        int s = half;
-        for (; s + 6 < n; s += 8) {
-            o0 = fmaf(pc[(int64_t)s * HD], sW[s], o0);
-            o1 = fmaf(pc[(int64_t)(s + 2) * HD], sW[s + 2], o1);
-            o2 = fmaf(pc[(int64_t)(s + 4) * HD], sW[s + 4], o2);
-            o3 = fmaf(pc[(int64_t)(s + 6) * HD], sW[s + 6], o3);
+#pragma unroll
+        for (int i = 0; i < kPerThread; i += 4) {
+            o0 = fmaf(ov[i], sW[half + 2 * i], o0);
+            o1 = fmaf(ov[i + 1], sW[half + 2 * i + 2], o1);
+            o2 = fmaf(ov[i + 2], sW[half + 2 * i + 4], o2);
+            o3 = fmaf(ov[i + 3], sW[half + 2 * i + 6], o3);
         }
-        for (; s < n; s += 2) o0 = fmaf(pc[(int64_t)s * HD], sW[s], o0);
+        if (c0 + kSplitChunk < ns) request(c0 + kSplitChunk);
     }
     l = wave_sum(l);
     __syncthreads();
