@@ -313,7 +313,7 @@ def plain_read_reference(torch, tensors, steps, warmup):
     """A same-box reference for the decode attention's bandwidth: one plain streaming read of
     the same bytes, torch.sum over rows of 4096 bf16 values into fp32 (one small output per row),
     timed like a step.  Returns ms per pass over all the tensors."""
-    views = [t.view(-1, 4096) for t in tensors]
+    views = [t.view(-1, 4096 if t.numel() % 4096 == 0 else t.shape[-1]) for t in tensors]
 
     def run():
         for v in views:
