@@ -313,6 +313,34 @@ def test_bf16_decode_matches_oracle_ragged(hq, hkv):
     check_decode_steps(gl, ws, lens, kd, vd)
 
 
+def test_bf16_decode_long_caches_merge_in_chunks():
+    """Decode over caches longer than 64 splits of 1024 keys: the merge of the splits requests the
+    partial outputs of 64 splits per chunk, so 70,000 and 131,072 cached keys (69 and 129 splits:
+    two and three chunks) take its chunk loop; a third sequence with 32,768 (33 splits, one
+    chunk) shares the call.  Every output row against the oracle decode.  (The layer is declared
+    with a 256K-position context; the default 40,960 rejects these positions before any launch.)"""
+    cfg = small_bf16_cfg(hq=4, hkv=2, max_position_embeddings=262144)
+    gl = GpuLayer.seeded(cfg, seed=31)
+    lens = [70000, 131072, 32768]
+    b, hkv, d = len(lens), cfg.num_key_value_heads, cfg.head_dim
+    cap = max(lens) + 1
+    log(f"bf16 decode over long caches, lens {lens}")
+    kd = torch.zeros((b, hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vd = torch.zeros_like(kd)
+    kcs, vcs = [], []
+    for i, n in enumerate(lens):
+        kb = np.stack([si.cache_block(cfg, "k", i, h, n, seed=31) for h in range(hkv)])
+        vb = np.stack([si.cache_block(cfg, "v", i, h, n, seed=31) for h in range(hkv)])
+        kd[i, :, :n] = to_dev(kb, cfg)
+        vd[i, :, :n] = to_dev(vb, cfg)
+        kcs.append(kb)
+        vcs.append(vb)
+    x = si.layer_input(cfg, b, 1, seed=31)
+    y, _ = gl.decode(to_dev(x, cfg), lens, kd, vd)
+    ref, _, _ = oracle.layer_decode(x, gl.w_np, cfg, kcs, vcs, lens)
+    assert_bf16_parity(to_np(y), ref, "decode y over 69, 129 and 33 splits")
+
+
 @pytest.mark.parametrize("b", [1, 5, 16])
 def test_bf16_decode_skinny_kernels(b):
     """Decode at widths where the skinny projections take their whole-line LDS-staged form (o and
