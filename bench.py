@@ -309,6 +309,30 @@ def bench_stack(torch, si, nat, wl, steps, warmup):
             "kernels": kernel_table(avg, flops)}
 
 
+def mfma_ceiling(torch, nat, launches=3, workgroups=1024, iterations=20000):
+    """Rate of the matrix-core probe (qwen3_probe_mfma_rate): back-to-back bf16 32x32x16 MFMAs on
+    register operands, no memory traffic.  The GEMMs' achieved rate is also given as a fraction of
+    this measured ceiling beside the published peak."""
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    nat.probe_mfma_rate(out, workgroups, iterations)   # warm-up launch
+    flops = workgroups * 4 * iterations * 16 * 32768   # 32 x 32 x 16 multiply-adds per MFMA
+    best = None
+    for _ in range(launches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nat.probe_mfma_rate(out, workgroups, iterations)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    if not torch.isfinite(out).all():
+        raise RuntimeError("matrix-core probe produced non-finite sums")
+    tf = flops / (best * 1e-3) / 1e12
+    return {"probe": "qwen3_probe_mfma_rate (bf16 32x32x16 MFMAs on register operands)",
+            "workgroups": workgroups, "iterations": iterations, "ms": round(best, 4), "tflops": round(tf, 1),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def plain_read_reference(torch, tensors, steps, warmup):
     """A same-box reference for the decode attention's bandwidth: one plain streaming read of
     the same bytes, torch.sum over rows of 4096 bf16 values into fp32 (one small output per row),
@@ -794,6 +818,8 @@ def main():
 
     head = records["c4"]
     wl4 = wls["c4"]
+    ceiling = mfma_ceiling(torch, nat)
+    ceiling["kernel_frac_of_ceiling"] = round(head["roofline"]["achieved"] / ceiling["tflops"], 4)
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -813,7 +839,7 @@ def main():
                    "hidden_size": wl4.cfg.hidden_size,
                    "heads": [wl4.cfg.num_attention_heads, wl4.cfg.num_key_value_heads],
                    "head_dim": wl4.cfg.head_dim, "intermediate_size": wl4.cfg.intermediate_size},
-        "roofline": head["roofline"],
+        "roofline": dict(head["roofline"], mfma_ceiling=ceiling),
         "layer_tflops": head["layer_tflops"],
         "layer_frac_of_bf16_peak": head["layer_frac_of_bf16_peak"],
         "kernels": head["kernels"],

@@ -313,6 +313,19 @@ qwen3_status qwen3_rmsnorm_gain_offset(const void* x, const void* weight, void* 
                                        int32_t width, float eps, float gain_offset, qwen3_dtype dtype,
                                        void* stream);
 
+/* Matrix-core rate probe, a measurement aid and not a step of the layer: each
+ * of `workgroups` workgroups (4 waves) issues `iterations` x 16 back-to-back
+ * bf16 32x32x16 MFMAs (the GEMMs' instruction, 32 x 32 x 16 multiply-adds
+ * each) on pseudo-random operands held in registers, so the launch's rate is
+ * what the matrix cores sustain under the chip's power management with no
+ * memory or LDS traffic: the ceiling beside the published dense bf16 peak that
+ * the GEMMs' fraction can be read against.  Work per launch:
+ * workgroups x 4 x iterations x 16 x 32768 flops.  out: device buffer of
+ * workgroups x 256 floats (caller-owned), overwritten with one sum per lane.
+ * Asynchronous on `stream`.  Errors: INVALID_ARGUMENT (NULL out, workgroups
+ * or iterations < 1), DEVICE (launch failure). */
+qwen3_status qwen3_probe_mfma_rate(float* out, int32_t workgroups, int32_t iterations, void* stream);
+
 /* Per-kernel timing of prefill / decode calls made while profiling is on:
  * every launch is bracketed by two hipEvents on the call's stream. */
 typedef struct {

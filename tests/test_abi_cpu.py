@@ -311,3 +311,12 @@ def test_decode_noalloc_rejects_before_any_device_call(layer):
         nat.QWEN3_ERR_INVALID_ARGUMENT
     assert L.qwen3_layer_decode_noalloc(layer, FAKE, FAKE, 0, one, FAKE, FAKE, 16, None) == \
         nat.QWEN3_ERR_INVALID_ARGUMENT
+
+
+def test_mfma_probe_rejects_bad_arguments_before_any_launch():
+    L = nat.lib()
+    assert L.qwen3_probe_mfma_rate(None, 4, 4, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+    assert "non-NULL" in err()
+    for wg, it in [(0, 4), (4, 0), (-1, 4)]:
+        assert L.qwen3_probe_mfma_rate(FAKE, wg, it, None) == nat.QWEN3_ERR_INVALID_ARGUMENT
+        assert "positive" in err()

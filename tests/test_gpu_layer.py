@@ -485,3 +485,19 @@ def test_profiling_reports_every_stage():
         launches, ms = prof[n]
         assert launches == 3 and ms > 0
     assert gl.layer.read_profile() == {}
+
+
+def test_mfma_probe_runs_and_repeats_exactly():
+    """The matrix-core rate probe: finite per-lane sums, identical over two launches (the same
+    MFMAs on the same register operands in the same order)."""
+    import torch
+    from transformer_decoder_layer_rmsnorm_amd import _native as nat
+    log("mfma probe: 8 workgroups x 50 iterations, twice")
+    a = torch.empty(8 * 256, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    nat.probe_mfma_rate(a, 8, 50)
+    nat.probe_mfma_rate(b, 8, 50)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all()
+    assert torch.equal(a, b)
+    assert a.abs().max().item() > 0

@@ -29,7 +29,7 @@ EXPORTED = (
     "qwen3_layer_prefill_padded", "qwen3_layer_prefill_window", "qwen3_layer_decode",
     "qwen3_layer_decode_padded", "qwen3_layer_decode_window", "qwen3_layer_decode_noalloc",
     "qwen3_rmsnorm", "qwen3_rmsnorm_gain_offset", "qwen3_layer_set_profiling", "qwen3_layer_read_profile",
-    "qwen3_status_string", "qwen3_last_error",
+    "qwen3_probe_mfma_rate", "qwen3_status_string", "qwen3_last_error",
 )
 
 WEIGHT_NAMES = (
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
         "qwen3_rmsnorm": ([P, P, P, I64, I32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_rmsnorm_gain_offset": ([P, P, P, I64, I32, F32, F32, ctypes.c_int, P], ctypes.c_int),
         "qwen3_layer_set_profiling": ([P, I32], ctypes.c_int),
+        "qwen3_probe_mfma_rate": ([P, I32, I32, P], ctypes.c_int),
         "qwen3_layer_read_profile": ([P, ctypes.POINTER(StageTime), I32, ctypes.POINTER(I32)], ctypes.c_int),
         "qwen3_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "qwen3_last_error": ([], ctypes.c_char_p),
@@ -254,6 +255,15 @@ class Layer:
         n = ctypes.c_int32()
         check(lib().qwen3_layer_read_profile(self._h, buf, 32, ctypes.byref(n)), "qwen3_layer_read_profile")
         return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(n.value)}
+
+
+def probe_mfma_rate(out, workgroups: int, iterations: int, stream=None) -> None:
+    """Matrix-core rate probe (qwen3_probe_mfma_rate): out is a float32 CUDA tensor of at least
+    workgroups * 256 elements."""
+    if out.dtype != torch.float32 or out.numel() < workgroups * 256 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of at least workgroups * 256 elements")
+    check(lib().qwen3_probe_mfma_rate(_ptr(out), int(workgroups), int(iterations), _stream(stream)),
+          "qwen3_probe_mfma_rate")
 
 
 def rmsnorm(x, weight, y, eps: float, stream=None, gain_offset: float = 0.0) -> None:

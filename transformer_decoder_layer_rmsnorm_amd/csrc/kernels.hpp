@@ -201,4 +201,8 @@ hipError_t launch_attention_decode_split_bf16(const DecodeAttnArgs& args, hipStr
 hipError_t launch_attention_decode_combine_bf16(const DecodeAttnArgs& args, hipStream_t stream);
 constexpr int kDecodeSplitKeys = 1024;
 
+// Matrix-core rate probe (mfma_probe.hip): workgroups x 4 waves, each iters x 16 bf16 32x32x16
+// MFMAs on register operands; out receives workgroups x 256 floats.
+hipError_t launch_mfma_probe(float* out, int workgroups, int iters, hipStream_t stream);
+
 }  // namespace q3

@@ -791,6 +791,16 @@ qwen3_status qwen3_rmsnorm_gain_offset(const void* x, const void* weight, void* 
     return QWEN3_OK;
 }
 
+qwen3_status qwen3_probe_mfma_rate(float* out, int32_t workgroups, int32_t iterations, void* stream) {
+    if (!out) return fail(QWEN3_ERR_INVALID_ARGUMENT, "out must be non-NULL");
+    if (workgroups < 1 || iterations < 1)
+        return fail(QWEN3_ERR_INVALID_ARGUMENT, "workgroups (%d) and iterations (%d) must be positive", workgroups,
+                    iterations);
+    const hipError_t e = launch_mfma_probe(out, workgroups, iterations, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QWEN3_ERR_DEVICE, "mfma probe: %s", hipGetErrorString(e));
+    return QWEN3_OK;
+}
+
 qwen3_status qwen3_layer_set_profiling(qwen3_layer* L, int32_t enabled) {
     if (!L) return fail(QWEN3_ERR_INVALID_ARGUMENT, "layer is NULL");
     L->profiling = enabled != 0;
